@@ -1,0 +1,285 @@
+"""CPU oracle of the Jano per-step hot path -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously correct NumPy code. Only the tests, the smoke check and
+the bench's CPU-baseline leg may import it; the product path (the HIP library
+and its Python binding) never does, and shares no code with it.
+
+Citations name the Jano summary pages on gist.science (one per language:
+nl, fr, pt, zh, ko; all titled "Jano: Adaptive Diffusion Generation with
+Early-stage Convergence Awareness") and the section of their technical summary.
+
+Readings taken where the pages are silent (each is listed in the design notes):
+  * the analyzer differences the gradient fields along the STEP axis (second
+    order), using forward differences without padding; gradient pairs may cross
+    into the neighbouring block (one-cell halo);
+  * the block score is the mean absolute value over every valid
+    (axis, step, channel, position) term that starts inside the block;
+  * levels are rank quantiles: lowest static_permille of blocks -> 1 (Static),
+    next moderate_permille -> 2 (Moderate), rest -> 3 (Active); ties by id;
+  * a token is due at step s if s is a warm-up or cool-down step, else if
+    (s - W) is a multiple of its level's period; index lists are ascending;
+  * attention is non-causal softmax(Q K^T / sqrt(d)) V per head, over the
+    whole full-sequence cache after the fresh rows were written into it.
+
+Every function below is pinned by tests/test_oracle_pins.py against closed
+forms, invariants and brute force; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+STATIC, MODERATE, ACTIVE = 1, 2, 3
+
+
+# --------------------------------------------------------------------------
+# Analyzer: block-wise complexity score.
+# Jano pages: [zh] technical summary §2.1 (block-wise complexity analyzer:
+# 3D frame x height x width blocks, temporal and spatial gradients, second
+# order difference over the first K steps, a complexity score per block);
+# [nl] methodology §1; [fr] §2.A; [pt] §2.A; [ko] §2.A.
+# --------------------------------------------------------------------------
+
+def block_grid(F: int, H: int, W: int, block) -> tuple:
+    bF, bH, bW = block
+    return (-(-F // bF), -(-H // bH), -(-W // bW))
+
+
+def _block_ids(F, H, W, block, nB):
+    bF, bH, bW = block
+    _, nBH, nBW = nB
+    f = np.arange(F) // bF
+    h = np.arange(H) // bH
+    w = np.arange(W) // bW
+    return (f[:, None, None] * nBH + h[None, :, None]) * nBW + w[None, None, :]
+
+
+def step_second_difference(lat: np.ndarray) -> np.ndarray:
+    """D_k = L_{k+1} - 2 L_k + L_{k-1}, k = 1..K-2, in fp64 (exact for fp32 L)."""
+    L = np.asarray(lat, dtype=np.float64)
+    return L[2:] - 2.0 * L[1:-1] + L[:-2]
+
+
+def analyze_scores(lat: np.ndarray, block) -> np.ndarray:
+    """Per-block complexity score rounded to fp32 [B] (see analyze_scores_f64)."""
+    return analyze_scores_f64(lat, block).astype(np.float32)
+
+
+def analyze_scores_f64(lat: np.ndarray, block) -> np.ndarray:
+    """Per-block complexity score, fp64 [B].
+
+    lat: fp32 [K, C, F, H, W], the latents entering steps 0..K-1 (K >= 3).
+    The gradient of x along axis a at p is x(p + e_a) - x(p); its second step
+    difference equals D_k(p + e_a) - D_k(p) by linearity. The score of block b
+    is the mean |.| of those terms over all axes a with extent >= 2, all
+    k = 1..K-2, all channels and all p in b with p + e_a inside the latent."""
+    K, C, F, H, W = lat.shape
+    if K < 3:
+        raise ValueError("need K >= 3 warm-up latents")
+    D = step_second_difference(lat)               # [K-2, C, F, H, W]
+    nB = block_grid(F, H, W, block)
+    B = nB[0] * nB[1] * nB[2]
+    bid = _block_ids(F, H, W, block, nB)
+    total = np.zeros(B, dtype=np.float64)
+    count = np.zeros(B, dtype=np.float64)
+    for axis in (2, 3, 4):                        # F (temporal), H, W (spatial)
+        ext = D.shape[axis]
+        if ext < 2:
+            continue
+        E = np.abs(np.diff(D, axis=axis))         # D(p + e_a) - D(p)
+        per_pos = E.sum(axis=(0, 1))              # sum over k and c -> [F', H', W']
+        sl = [slice(None)] * 3
+        sl[axis - 2] = slice(0, ext - 1)          # positions p with p + e_a valid
+        ids = bid[tuple(sl)]
+        total += np.bincount(ids.ravel(), weights=per_pos.ravel(), minlength=B)
+        count += np.bincount(ids.ravel(), minlength=B) * float(D.shape[0] * C)
+    return np.where(count > 0, total / np.where(count > 0, count, 1.0), 0.0)
+
+
+def analyze_scores_bruteforce(lat: np.ndarray, block) -> np.ndarray:
+    """The same definition as plain nested loops, fp64 [B] (tiny inputs only)."""
+    K, C, F, H, W = lat.shape
+    nB = block_grid(F, H, W, block)
+    B = nB[0] * nB[1] * nB[2]
+    tot = [0.0] * B
+    cnt = [0] * B
+    bF, bH, bW = block
+
+    def x(k, c, f, h, w):
+        return float(lat[k, c, f, h, w])
+
+    for f in range(F):
+        for h in range(H):
+            for w in range(W):
+                b = ((f // bF) * nB[1] + h // bH) * nB[2] + w // bW
+                for (df, dh, dw) in ((1, 0, 0), (0, 1, 0), (0, 0, 1)):
+                    f2, h2, w2 = f + df, h + dh, w + dw
+                    if f2 >= F or h2 >= H or w2 >= W:
+                        continue
+                    for c in range(C):
+                        for k in range(1, K - 1):
+                            g_next = x(k + 1, c, f2, h2, w2) - x(k + 1, c, f, h, w)
+                            g_cur = x(k, c, f2, h2, w2) - x(k, c, f, h, w)
+                            g_prev = x(k - 1, c, f2, h2, w2) - x(k - 1, c, f, h, w)
+                            tot[b] += abs(g_next - 2.0 * g_cur + g_prev)
+                            cnt[b] += 1
+    return np.array([t / n if n else 0.0 for t, n in zip(tot, cnt)], dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Levels. Jano pages: [nl] methodology §1 (three convergence levels:
+# Static, Moderate, Active); [zh] §2.2 item 1; [ko] §2.B.
+# --------------------------------------------------------------------------
+
+def level_split(B: int, static_permille: int, moderate_permille: int) -> tuple:
+    """(nS, nSM): blocks of rank < nS are Static, rank < nSM Moderate."""
+    nS = (static_permille * B + 500) // 1000
+    nSM = ((static_permille + moderate_permille) * B + 500) // 1000
+    return nS, nSM
+
+
+def assign_levels(scores: np.ndarray, static_permille: int = 400,
+                  moderate_permille: int = 300) -> np.ndarray:
+    scores = np.asarray(scores, dtype=np.float32)
+    B = scores.shape[0]
+    order = np.lexsort((np.arange(B), scores))    # by score, then block id
+    rank = np.empty(B, dtype=np.int64)
+    rank[order] = np.arange(B)
+    nS, nSM = level_split(B, static_permille, moderate_permille)
+    lv = np.full(B, ACTIVE, dtype=np.uint8)
+    lv[rank < nSM] = MODERATE
+    lv[rank < nS] = STATIC
+    return lv
+
+
+def token_block_ids(latent_fhw, patch, block) -> np.ndarray:
+    """Block id of every token in token-major order n = (f*Ht + h)*Wt + w.
+    Token (f, h, w) starts at latent pixel (f*pF, h*pH, w*pW)."""
+    F, H, W = latent_fhw
+    pF, pH, pW = patch
+    bF, bH, bW = block
+    nB = block_grid(F, H, W, block)
+    Ft, Ht, Wt = F // pF, H // pH, W // pW
+    bf = (np.arange(Ft) * pF) // bF
+    bh = (np.arange(Ht) * pH) // bH
+    bw = (np.arange(Wt) * pW) // bW
+    ids = (bf[:, None, None] * nB[1] + bh[None, :, None]) * nB[2] + bw[None, None, :]
+    return ids.ravel()
+
+
+def token_levels(levels: np.ndarray, latent_fhw, patch, block) -> np.ndarray:
+    return np.asarray(levels, dtype=np.uint8)[token_block_ids(latent_fhw, patch, block)]
+
+
+def level_token_counts(levels, latent_fhw, patch, block) -> np.ndarray:
+    tl = token_levels(levels, latent_fhw, patch, block)
+    return np.array([(tl == v).sum() for v in (STATIC, MODERATE, ACTIVE)], dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Schedule. Jano pages: [nl] methodology §2 (warm-up, interleaved generation
+# with per-level update frequency, cool-down); [zh] §2.2 item 2; [pt] §2.B.
+# --------------------------------------------------------------------------
+
+def is_dense_step(step: int, T: int, W: int, Cd: int) -> bool:
+    return step < W or step >= T - Cd
+
+
+def active_mask(tok_levels: np.ndarray, step: int, T: int, W: int, Cd: int,
+                periods=(4, 2, 1)) -> np.ndarray:
+    tl = np.asarray(tok_levels)
+    if is_dense_step(step, T, W, Cd):
+        return np.ones(tl.shape[0], dtype=bool)
+    due = np.zeros(tl.shape[0], dtype=bool)
+    for lv, p in zip((STATIC, MODERATE, ACTIVE), periods):
+        if (step - W) % p == 0:
+            due |= tl == lv
+    return due
+
+
+def schedule(tok_levels, step, T, W, Cd, periods=(4, 2, 1)) -> np.ndarray:
+    """Ascending int32 indices of the tokens computed at this step."""
+    return np.flatnonzero(active_mask(tok_levels, step, T, W, Cd, periods)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Token activation and the full-sequence KV cache. Jano pages: [nl]
+# methodology §2 (KV cache of frozen tokens; cached pairs combined with the
+# active queries without restoring positions, correct because attention does
+# not depend on key/value order); [zh] §2.2 item 3; [fr] §2.B.
+# --------------------------------------------------------------------------
+
+def gather_rows(X: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    return np.asarray(X)[np.asarray(idx, dtype=np.int64)]
+
+
+def scatter_rows(cache: np.ndarray, idx: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    out = np.array(cache, copy=True)
+    out[np.asarray(idx, dtype=np.int64)] = rows
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns (uint16) exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float | None = None,
+              dtype=np.float64, q_chunk: int = 2048) -> np.ndarray:
+    """Non-causal softmax attention per head.
+
+    Q [n, H, d], K and V [N, H, d] (float). Returns [n, H, d] in `dtype`.
+    out[i, h] = sum_j softmax_j(Q[i,h] . K[j,h] * scale) V[j,h]; each query row
+    is independent, so rows are evaluated in chunks to bound memory."""
+    n, Hh, d = Q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    Q = np.asarray(Q, dtype=dtype)
+    K = np.asarray(K, dtype=dtype)
+    V = np.asarray(V, dtype=dtype)
+    out = np.empty((n, Hh, d), dtype=dtype)
+    for h in range(Hh):
+        Kh = np.ascontiguousarray(K[:, h, :])
+        Vh = np.ascontiguousarray(V[:, h, :])
+        for i0 in range(0, n, q_chunk):
+            S = (Q[i0:i0 + q_chunk, h, :] @ Kh.T) * dtype(scale)
+            S -= S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            out[i0:i0 + q_chunk, h, :] = (P @ Vh) / P.sum(axis=1, keepdims=True)
+    return out
+
+
+def attention_bruteforce(Q, K, V, scale=None) -> np.ndarray:
+    """Scalar-loop fp64 attention for tiny inputs (no max shift needed there)."""
+    n, Hh, d = Q.shape
+    N = K.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n, Hh, d))
+    for h in range(Hh):
+        for i in range(n):
+            logits = [sum(float(Q[i, h, e]) * float(K[j, h, e]) for e in range(d)) * scale
+                      for j in range(N)]
+            m = max(logits)
+            wts = [np.exp(t - m) for t in logits]
+            z = sum(wts)
+            for e in range(d):
+                out[i, h, e] = sum(wts[j] * float(V[j, h, e]) for j in range(N)) / z
+    return out
+
+
+def attn_step(Q_act_bits, Knew_bits, Vnew_bits, idx, Kc_bits, Vc_bits, scale=None,
+              dtype=np.float64, queries=None):
+    """One interleaved attention step on bf16 bit-pattern inputs.
+
+    Writes the fresh K/V rows of the active tokens into the caches, then runs
+    the active queries against the whole cache. Returns (out, Kc', Vc') with
+    out in `dtype`; `queries` optionally restricts which active rows are
+    evaluated (sampled checks at large sizes)."""
+    Kc2 = scatter_rows(Kc_bits, idx, Knew_bits)
+    Vc2 = scatter_rows(Vc_bits, idx, Vnew_bits)
+    Q = bf16_to_f64(Q_act_bits)
+    if queries is not None:
+        Q = Q[np.asarray(queries)]
+    out = attention(Q, bf16_to_f64(Kc2), bf16_to_f64(Vc2), scale, dtype=dtype)
+    return out, Kc2, Vc2
