@@ -1,0 +1,178 @@
+/*
+ * jano.h -- C ABI of libjano, the MI355X (gfx950) hot path of Jano's
+ * convergence-adaptive DiT generation.
+ *
+ * Method: "Jano: Adaptive Diffusion Generation with Early-stage Convergence
+ * Awareness" as summarised on its gist.science pages (nl, fr, pt, zh, ko).
+ * Citations below name those pages by language and the section of their
+ * technical summary.
+ *
+ * Conventions (all entry points):
+ *   - Tensor arguments are DEVICE pointers to caller-owned memory, densely
+ *     packed (C order) with the layout given per argument. Structs and
+ *     scalar arguments are host values. bf16 data travels as uint16_t bits.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on that stream and returns without synchronising; kernel
+ *     faults surface at the caller's next synchronisation.
+ *   - Return value: JANO_OK (0) or a negative JANO_E_* code. Arguments are
+ *     validated on the host before anything is enqueued; on a non-zero return
+ *     nothing was launched and no output was written (except JANO_E_HIP,
+ *     reported when a launch itself fails).
+ *   - The library allocates no device memory and keeps no state between
+ *     calls; calls on different streams may run concurrently as long as their
+ *     outputs do not overlap.
+ */
+#ifndef JANO_H
+#define JANO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JANO_ABI_VERSION 1
+
+enum {
+  JANO_OK = 0,
+  JANO_E_INVAL = -1,       /* null pointer, bad size, inconsistent geometry */
+  JANO_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim)     */
+  JANO_E_RANGE = -3,       /* index list out of range / not ascending       */
+  JANO_E_WORKSPACE = -4,   /* workspace missing or too small                */
+  JANO_E_HIP = -5          /* a HIP launch reported an error                */
+};
+
+/* Latent history and token geometry.
+ *   K x [C, F, H, W]  warm-up latents (K >= 3), fp32
+ *   (bF, bH, bW)      analyzer block in latent pixels (frame x height x width)
+ *   (pF, pH, pW)      patch: latent pixels per token; F, H, W must be
+ *                     multiples of the patch and each block dimension a
+ *                     multiple of the patch dimension.
+ * Tokens form the grid (F/pF, H/pH, W/pW) in order n = (f*Ht + h)*Wt + w;
+ * blocks form the grid ceil(F/bF) x ceil(H/bH) x ceil(W/bW) in order
+ * b = (bf*nBH + bh)*nBW + bw (edge blocks may be ragged). */
+typedef struct jano_grid {
+  int32_t K, C, F, H, W;
+  int32_t bF, bH, bW;
+  int32_t pF, pH, pW;
+} jano_grid;
+
+/* Phases of the interleaved pipeline: steps [0, W) warm-up (dense),
+ * [T-Cd, T) cool-down (dense); in between a token of level L (1 Static,
+ * 2 Moderate, 3 Active) is recomputed when (step - W) % period[L-1] == 0. */
+typedef struct jano_sched {
+  int32_t T, W, Cd;
+  int32_t period[3];
+} jano_sched;
+
+int jano_abi_version(void);
+const char *jano_status_string(int status);
+
+/* Host helpers (no device access): number of analyzer blocks and tokens. */
+int jano_grid_sizes(const jano_grid *g, int64_t *num_blocks, int64_t *num_tokens);
+
+/* Host helper: number of tokens jano_schedule selects at `step`, from the
+ * per-level token counts (host copy of jano_analyze's level_tok_counts). */
+int jano_schedule_count(const int32_t *level_tok_counts_host, const jano_sched *sc,
+                        int step, int64_t *n_act);
+
+/* Device workspace jano_analyze needs, in bytes (0 on invalid geometry). */
+size_t jano_analyze_workspace_bytes(const jano_grid *g);
+
+/*
+ * jano_analyze -- block-wise complexity analyzer plus level bucketing.
+ * Pages: zh technical summary §2.1 (3D blocks, temporal and spatial gradients,
+ * second-order difference over the first K steps, one score per block);
+ * nl methodology §1 (three convergence levels); fr/pt/ko §2.A.
+ *
+ *   lat               [K][C][F][H][W] fp32, the latents entering steps 0..K-1
+ *   static_permille,  share of blocks (per mille, rounded half up) assigned
+ *   moderate_permille Static (lowest scores) and Moderate (next); the rest are
+ *                     Active. Each in [0, 1000], sum <= 1000.
+ *   scores   (out)    [B] fp32: mean |D_k(p+e_a) - D_k(p)| over the axes a
+ *                     with extent >= 2, k = 1..K-2, all channels and every p
+ *                     in the block with p+e_a inside the latent, where
+ *                     D_k = L_{k+1} - 2 L_k + L_{k-1} (formed in fp64)
+ *   levels   (out)    [B] uint8 in {1,2,3}: blocks ranked by (score, id)
+ *   level_tok_counts (out) [3] int32: tokens at level 1, 2, 3
+ *   ws, ws_bytes      device workspace of >= jano_analyze_workspace_bytes
+ *                     (contents need no initialisation)
+ */
+int jano_analyze(const float *lat, const jano_grid *g, int static_permille,
+                 int moderate_permille, float *scores, uint8_t *levels,
+                 int32_t *level_tok_counts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * jano_schedule -- active index list of one denoising step.
+ * Pages: nl methodology §2 (warm-up, interleaved generation with per-level
+ * update frequency, cool-down); zh §2.2 item 2; pt/fr/ko §2.B.
+ *
+ *   levels   [B] uint8 block levels (from jano_analyze)
+ *   idx      (out) int32 [capacity >= N]: ascending token indices due at
+ *            `step`; entries past n_act are left untouched
+ *   n_act_dev (out) one int32 on the device: number of indices written
+ *   0 <= step < T.
+ */
+int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *sc,
+                  int step, int32_t *idx, int32_t *n_act_dev, void *stream);
+
+/*
+ * jano_gather_rows -- adaptive token activation: X_act[i,:] = X[idx[i],:].
+ * Pages: nl contributions item 2 (adaptive token activation); zh §3 item 2.
+ *   X [N][D] bf16, idx [n_act] int32 in [0, N), X_act (out) [n_act][D] bf16.
+ * Bit-exact copy. n_act == 0 is a no-op.
+ */
+int jano_gather_rows(const uint16_t *X, int64_t N, int64_t D, const int32_t *idx,
+                     int64_t n_act, uint16_t *X_act, void *stream);
+
+/*
+ * jano_scatter_kv -- write fresh K/V rows of the active tokens into the
+ * full-sequence cache: Kc[idx[i]] = K_new[i], Vc[idx[i]] = V_new[i].
+ * Pages: nl methodology §2 (KV cache of frozen tokens); zh §2.2 item 3.
+ *   K_new, V_new [n_act][H*d] bf16; Kc, Vc [N][H*d] bf16, updated in place.
+ *   idx must hold distinct indices (duplicates race).
+ */
+int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t *idx,
+                    int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int64_t HD,
+                    void *stream);
+
+/*
+ * jano_attention -- non-causal softmax attention of n_q queries against all
+ * N cached keys/values, per head: out[i,h] = softmax(Q[i,h] Kc[:,h]^T * scale) Vc[:,h].
+ * Pages: full attention over all tokens, quadratic in sequence length
+ * (nl problem statement; fr §1); order of keys/values is irrelevant
+ * (nl methodology §2).
+ *   Q [n_q][H][d], Kc, Vc [N][H][d], out (out) [n_q][H][d], all bf16;
+ *   d in {64, 128}; scale <= 0 selects 1/sqrt(d). bf16 MFMA products, fp32
+ *   accumulation and online softmax. n_q == 0 is a no-op; N >= 1.
+ */
+int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
+                   int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
+
+/*
+ * jano_attn_step -- one interleaved-step attention: jano_scatter_kv of the
+ * fresh rows into the cache, then jano_attention of the active queries against
+ * the whole cache, on one stream (the scatter completes before attention reads).
+ * Pages: nl methodology §2 (cached pairs of frozen tokens combined with the
+ * active queries without restoring positions); zh §2.2 item 3; pt §2.B.
+ *   Q_act, K_new, V_new [n_act][H][d]; idx [n_act] ascending distinct in [0,N);
+ *   Kc, Vc [N][H][d] in/out; out (out) [n_act][H][d].
+ */
+int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
+                   const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc,
+                   int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
+
+/*
+ * jano_check_idx -- validate an index list on the device: writes 0 to
+ * *flag_dev when idx is strictly ascending within [0, N), else JANO_E_RANGE.
+ * Debug aid for the precondition of jano_scatter_kv / jano_attn_step.
+ */
+int jano_check_idx(const int32_t *idx, int64_t n_act, int64_t N, int32_t *flag_dev,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JANO_H */

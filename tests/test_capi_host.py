@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/jano.h declares, and rejects bad arguments before touching a GPU.
+No kernel is launched here (runs on machines without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from token_sparse_attention_block_amd import configs, jano
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jano.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(jano.LIB_PATH),
+                                reason="libjano.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(jano_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_functions() == sorted(jano.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", jano.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+    L = jano.lib()
+    for name in declared_functions():
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings():
+    assert jano.abi_version() == 1
+    L = jano.lib()
+    assert L.jano_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert L.jano_status_string(code) not in (b"ok", b"unknown status")
+
+
+@pytest.mark.parametrize("cfg", list(configs.CONFIGS.values()), ids=lambda c: c.name)
+def test_grid_sizes_match_configs(cfg):
+    B, N = jano.grid_sizes(jano.GridSpec.of(cfg))
+    assert (B, N) == (cfg.B, cfg.N)
+    # one fp64 partial per (channel, strip, block)
+    ws = jano.analyze_workspace_bytes(jano.GridSpec.of(cfg))
+    assert ws >= cfg.C * cfg.B * 8
+
+
+def test_known_block_and_token_counts():
+    assert jano.grid_sizes(jano.GridSpec.of(configs.V720)) == (5040, 75600)
+    assert jano.grid_sizes(jano.GridSpec.of(configs.V480)) == (2184, 32760)
+    assert jano.grid_sizes(jano.GridSpec.of(configs.IMAGE)) == (256, 4096)
+    assert jano.grid_sizes(jano.GridSpec.of(configs.TINY)) == (48, 768)
+
+
+def test_schedule_count_closed_form():
+    counts = (40, 30, 30)
+    got = [jano.schedule_count(counts, 50, 5, 5, (4, 2, 1), s) for s in range(50)]
+    assert got[:5] == [100] * 5 and got[45:] == [100] * 5
+    assert got[5:9] == [100, 30, 60, 30]
+    assert sum(got) == 10 * 100 + 10 * 100 + 10 * 30 + 10 * 60 + 10 * 30
+
+
+def _grid(**kw):
+    base = dict(K=5, C=16, F=21, H=90, W=160, bF=1, bH=8, bW=8, pF=1, pH=2, pW=2)
+    base.update(kw)
+    return jano.Grid(*[base[n] for n in ("K", "C", "F", "H", "W", "bF", "bH", "bW", "pF", "pH", "pW")])
+
+
+@pytest.mark.parametrize("kw", [dict(K=2), dict(C=0), dict(H=91), dict(bH=7), dict(pW=3),
+                                dict(bW=0), dict(F=-1)])
+def test_bad_geometry_rejected(kw):
+    L = jano.lib()
+    g = _grid(**kw)
+    B, N = ctypes.c_int64(), ctypes.c_int64()
+    assert L.jano_grid_sizes(ctypes.byref(g), ctypes.byref(B), ctypes.byref(N)) == jano.JANO_E_INVAL
+    assert L.jano_analyze_workspace_bytes(ctypes.byref(g)) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, fake, 1 << 30,
+                          None) == jano.JANO_E_INVAL
+
+
+def test_analyze_argument_errors():
+    L = jano.lib()
+    g = _grid()
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    ws = L.jano_analyze_workspace_bytes(ctypes.byref(g))
+    assert ws > 0
+    assert L.jano_analyze(null, ctypes.byref(g), 400, 300, fake, fake, fake, fake, ws, None) == -1
+    assert L.jano_analyze(fake, ctypes.byref(g), 700, 400, fake, fake, fake, fake, ws, None) == -1
+    assert L.jano_analyze(fake, ctypes.byref(g), -1, 300, fake, fake, fake, fake, ws, None) == -1
+    assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, fake, ws - 1, None) == -4
+    assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, null, ws, None) == -4
+
+
+def test_schedule_argument_errors():
+    L = jano.lib()
+    g = _grid()
+    fake = ctypes.c_void_p(0x1000)
+    sc = jano.Sched(50, 5, 5, (ctypes.c_int32 * 3)(4, 2, 1))
+    assert L.jano_schedule(fake, ctypes.byref(g), ctypes.byref(sc), 50, fake, fake, None) == -1
+    assert L.jano_schedule(fake, ctypes.byref(g), ctypes.byref(sc), -1, fake, fake, None) == -1
+    bad = jano.Sched(50, 5, 5, (ctypes.c_int32 * 3)(0, 2, 1))
+    assert L.jano_schedule(fake, ctypes.byref(g), ctypes.byref(bad), 7, fake, fake, None) == -1
+    bad2 = jano.Sched(8, 5, 5, (ctypes.c_int32 * 3)(4, 2, 1))
+    assert L.jano_schedule(fake, ctypes.byref(g), ctypes.byref(bad2), 1, fake, fake, None) == -1
+    assert L.jano_schedule(fake, ctypes.byref(g), ctypes.byref(sc), 7, ctypes.c_void_p(0), fake, None) == -1
+
+
+def test_rows_and_attention_argument_errors():
+    L = jano.lib()
+    f = ctypes.c_void_p(0x1000)
+    n = ctypes.c_void_p(0)
+    # gather
+    assert L.jano_gather_rows(f, 0, 8, f, 1, f, None) == -1
+    assert L.jano_gather_rows(f, 10, 8, n, 1, f, None) == -1
+    assert L.jano_gather_rows(n, 10, 8, n, 0, n, None) == 0          # empty is a no-op
+    # scatter: n_act > N, null cache
+    assert L.jano_scatter_kv(f, f, f, 11, f, f, 10, 8, None) == -1
+    assert L.jano_scatter_kv(f, f, f, 5, n, f, 10, 8, None) == -1
+    assert L.jano_scatter_kv(n, n, n, 0, f, f, 10, 8, None) == 0
+    # attention: unsupported head dim, misaligned pointer, bad sizes
+    assert L.jano_attention(f, 4, f, f, 10, 2, 96, 0.0, f, None) == -2
+    assert L.jano_attention(ctypes.c_void_p(0x1002), 4, f, f, 10, 2, 64, 0.0, f, None) == -1
+    assert L.jano_attention(f, 4, f, f, 0, 2, 64, 0.0, f, None) == -1
+    assert L.jano_attention(f, 4, f, f, 10, 0, 64, 0.0, f, None) == -1
+    assert L.jano_attention(f, 4, f, f, 10, 2, 64, float("nan"), f, None) == -1
+    assert L.jano_attention(n, 0, f, f, 10, 2, 64, 0.0, n, None) == 0
+    assert L.jano_attn_step(f, f, f, f, 11, f, f, 10, 2, 64, 0.0, f, None) == -1
+    assert L.jano_attn_step(f, f, f, f, 4, f, f, 10, 2, 80, 0.0, f, None) == -2
+    assert L.jano_attn_step(f, n, f, f, 4, f, f, 10, 2, 64, 0.0, f, None) == -1
+    assert L.jano_check_idx(f, 4, 10, n, None) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        jano.attention(x, x, x)
+    with pytest.raises(ValueError):
+        jano.analyze(torch.zeros(5, 16, 1, 16, 16), jano.GridSpec.of(configs.TINY))

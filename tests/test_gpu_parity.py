@@ -1,0 +1,337 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every kernel is fed the oracle's own inputs (e.g. the oracle's levels for the
+schedule, the oracle's index list for attention) so a mismatch is pinned to
+one kernel. Sizes span several tiles with ragged tails; the 720p cases run at
+the full size the bench times and are checked on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+from oracle import jano_oracle as O
+from token_sparse_attention_block_amd import configs, jano, synth
+
+from gpu_helpers import (SCORE_RTOL, assert_attn_close, dev, dev_bf16, host_bf16_f64, host_bits,
+                         threshold_band)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    jano.lib()  # fail loudly if the library is missing
+    return t
+
+
+def _idx_for(cfg, frac):
+    """Oracle index list of an Active-only interleaved step on a seeded map."""
+    lv = synth.active_level_map(cfg, frac)
+    tl = O.token_levels(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    sc = cfg.schedule
+    return O.schedule(tl, sc.W + 1, sc.T, sc.W, sc.Cd, sc.periods)
+
+
+# ------------------------------------------------------------- gather/scatter
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V720], ids=lambda c: c.name)
+def test_gather_rows_bit_exact(torch, cfg):
+    frac = cfg.active_fracs[0] if cfg.active_fracs else 0.25
+    print("gather", cfg.name, flush=True)
+    (Qb,) = synth.qkv_bits(cfg, which="q")
+    idx = _idx_for(cfg, 0.25 if cfg is configs.V720 else frac)
+    X = dev_bf16(Qb)
+    out = jano.gather_rows(X, dev(idx))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(out), O.gather_rows(Qb, idx))
+
+
+def test_gather_scalar_path_and_edges(torch):
+    rng = np.random.default_rng(3)
+    X = rng.integers(0, 65535, size=(37, 7), dtype=np.uint16)   # 14-byte rows -> scalar path
+    Xd = dev_bf16(X)
+    for idx in (np.array([36], np.int32), np.array([0, 5, 6, 36], np.int32),
+                np.arange(37, dtype=np.int32)):
+        out = jano.gather_rows(Xd, dev(idx))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out), X[idx])
+    empty = jano.gather_rows(Xd, dev(np.zeros(0, np.int32)))
+    assert empty.shape[0] == 0
+
+
+@pytest.mark.parametrize("cfg,frac", [(configs.TINY, 0.3), (configs.IMAGE, 0.3),
+                                      (configs.V720, 0.25), (configs.V720, 1.0)],
+                         ids=["tiny", "image", "720p-25", "720p-100"])
+def test_scatter_kv_bit_exact(torch, cfg, frac):
+    print("scatter", cfg.name, frac, flush=True)
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    idx = _idx_for(cfg, frac)
+    rng = np.random.default_rng(5)
+    Kn = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16)
+    Vn = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16)
+    Kc, Vc = dev_bf16(Kb), dev_bf16(Vb)
+    jano.scatter_kv(dev_bf16(Kn), dev_bf16(Vn), dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(Kc), O.scatter_rows(Kb, idx, Kn))
+    np.testing.assert_array_equal(host_bits(Vc), O.scatter_rows(Vb, idx, Vn))
+
+
+def test_scatter_scalar_path(torch):
+    rng = np.random.default_rng(6)
+    K = rng.integers(0, 65535, size=(20, 3, 3), dtype=np.uint16)   # 18-byte rows
+    V = rng.integers(0, 65535, size=(20, 3, 3), dtype=np.uint16)
+    idx = np.array([1, 2, 19], np.int32)
+    Kn = rng.integers(0, 65535, size=(3, 3, 3), dtype=np.uint16)
+    Kc, Vc = dev_bf16(K), dev_bf16(V)
+    jano.scatter_kv(dev_bf16(Kn), dev_bf16(Kn), dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(Kc), O.scatter_rows(K, idx, Kn))
+    np.testing.assert_array_equal(host_bits(Vc), O.scatter_rows(V, idx, Kn))
+
+
+# ------------------------------------------------------------------ analyzer
+
+def _analyze_gpu(torch, lat, spec, spm=400, mpm=300):
+    scores, levels, counts = jano.analyze(dev(lat), spec, spm, mpm)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), levels.cpu().numpy(), counts.cpu().numpy()
+
+
+def _check_analyzer(lat, spec, s_gpu, l_gpu, c_gpu, spm=400, mpm=300):
+    ref64 = O.analyze_scores_f64(lat, spec.block)
+    err = np.abs(s_gpu.astype(np.float64) - ref64)
+    bad = err > SCORE_RTOL * np.abs(ref64)
+    assert not bad.any(), ("scores", int(bad.sum()), float(err[bad].max()))
+    ref32 = ref64.astype(np.float32)
+    lv_ref = O.assign_levels(ref32, spm, mpm)
+    band = threshold_band(ref32, spm, mpm)
+    mism = (l_gpu != lv_ref) & ~band
+    assert not mism.any(), ("levels", np.flatnonzero(mism)[:10])
+    cnt = O.level_token_counts(l_gpu, (spec.F, spec.H, spec.W), spec.patch, spec.block)
+    np.testing.assert_array_equal(c_gpu, cnt)
+    return int(band.sum())
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V480, configs.V720],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("signal", [False, True], ids=["literal", "signal"])
+def test_analyzer_configs(torch, cfg, signal):
+    print("analyze", cfg.name, signal, flush=True)
+    lat = synth.latents(cfg, signal=signal)
+    spec = jano.GridSpec.of(cfg)
+    s, l, c = _analyze_gpu(torch, lat, spec, cfg.static_permille, cfg.moderate_permille)
+    nb = _check_analyzer(lat, spec, s, l, c, cfg.static_permille, cfg.moderate_permille)
+    print("  blocks in threshold band:", nb, flush=True)
+
+
+@pytest.mark.parametrize("shape,block,patch", [
+    ((5, 3, 4, 24, 40), (2, 8, 8), (1, 2, 2)),     # bF=2: frame pairs, F chunks
+    ((6, 2, 3, 18, 36), (1, 6, 12), (1, 2, 2)),    # R=2 strips (G=3), 12-lane segments
+    ((4, 2, 5, 30, 70), (1, 4, 4), (1, 1, 1)),     # several W chunks, ragged tail
+    ((3, 1, 1, 16, 16), (1, 4, 4), (1, 1, 1)),     # K=3, one frame
+    ((9, 2, 2, 8, 8), (1, 4, 4), (1, 1, 1)),       # K=9 -> generic kernel
+    ((5, 2, 2, 12, 140), (1, 4, 70), (1, 2, 2)),   # block wider than a wave -> generic
+    ((5, 2, 3, 9, 10), (1, 3, 5), (1, 1, 1)),      # odd block height -> generic
+])
+def test_analyzer_shapes(torch, shape, block, patch):
+    print("analyze shape", shape, block, flush=True)
+    rng = np.random.default_rng(sum(shape))
+    lat = rng.standard_normal(shape).astype(np.float32)
+    spec = jano.GridSpec(*shape, block=block, patch=patch)
+    s, l, c = _analyze_gpu(torch, lat, spec)
+    _check_analyzer(lat, spec, s, l, c)
+
+
+def test_analyzer_closed_forms(torch, golden):
+    # constant and step-affine latents score exactly zero
+    spec = jano.GridSpec(5, 3, 2, 8, 8, (1, 4, 4), (1, 1, 1))
+    s, l, c = _analyze_gpu(torch, np.full((5, 3, 2, 8, 8), 0.37, np.float32), spec)
+    assert np.all(s == 0.0)
+    assert l.tolist() == [1, 1, 1, 2, 2, 2, 3, 3]   # all ties -> by block id (nS=3, nSM=6)
+    rng = np.random.default_rng(1)
+    A = rng.integers(-1000, 1000, size=(3, 2, 8, 8)).astype(np.float64)
+    Bf = rng.integers(-1000, 1000, size=(3, 2, 8, 8)).astype(np.float64)
+    lat = np.stack([A + k * Bf for k in range(5)]).astype(np.float32)
+    s, _, _ = _analyze_gpu(torch, lat, spec)
+    assert np.all(s == 0.0)
+    # hand-derived impulse scores
+    g = golden("analyzer_impulse.json")
+    lat = np.zeros(g["shape"], dtype=np.float32)
+    i = g["impulse"]
+    lat[i["k"], i["c"], i["f"], i["h"], i["w"]] = 1.0
+    spec = jano.GridSpec(*g["shape"], block=tuple(g["block"]), patch=(1, 1, 1))
+    s, _, _ = _analyze_gpu(torch, lat, spec)
+    expect = np.zeros(g["num_blocks"], np.float32)
+    for b, (num, den) in g["expected_scores"].items():
+        expect[int(b)] = np.float32(num / den)
+    np.testing.assert_array_equal(s, expect)
+
+
+@pytest.mark.parametrize("spm,mpm", [(0, 0), (1000, 0), (0, 1000), (400, 600), (333, 333)])
+def test_analyzer_level_mixes(torch, spm, mpm):
+    cfg = configs.TINY
+    lat = synth.latents(cfg, signal=True)
+    spec = jano.GridSpec.of(cfg)
+    s, l, c = _analyze_gpu(torch, lat, spec, spm, mpm)
+    _check_analyzer(lat, spec, s, l, c, spm, mpm)
+
+
+# ------------------------------------------------------------------ schedule
+
+def test_schedule_all_steps_480p(torch):
+    cfg = configs.SCHED480
+    lat = synth.latents(cfg)
+    lv = O.assign_levels(O.analyze_scores(lat, cfg.block))
+    tl = O.token_levels(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    counts = O.level_token_counts(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    spec = jano.GridSpec.of(cfg)
+    sc = cfg.schedule
+    lvd = dev(lv)
+    idx_d = torch.full((cfg.N,), -7, dtype=torch.int32, device="cuda")
+    for s in range(sc.T):
+        idx, n = jano.schedule(lvd, spec, s, sc.T, sc.W, sc.Cd, sc.periods, idx=idx_d)
+        torch.cuda.synchronize()
+        ref = O.schedule(tl, s, sc.T, sc.W, sc.Cd, sc.periods)
+        n = int(n.item())
+        assert n == len(ref) == jano.schedule_count(counts, sc.T, sc.W, sc.Cd, sc.periods, s)
+        np.testing.assert_array_equal(idx.cpu().numpy()[:n], ref)
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V720], ids=lambda c: c.name)
+def test_schedule_random_levels(torch, cfg):
+    rng = np.random.default_rng(cfg.cfg_id)
+    lv = rng.integers(1, 4, size=cfg.B).astype(np.uint8)
+    tl = O.token_levels(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    spec = jano.GridSpec.of(cfg)
+    for s, periods in ((6, (4, 2, 1)), (7, (4, 2, 1)), (9, (4, 2, 1)), (11, (3, 5, 2)), (0, (4, 2, 1))):
+        idx, n = jano.schedule(dev(lv), spec, s, 50, 5, 5, periods)
+        torch.cuda.synchronize()
+        ref = O.schedule(tl, s, 50, 5, 5, periods)
+        assert int(n.item()) == len(ref)
+        np.testing.assert_array_equal(idx.cpu().numpy()[:len(ref)], ref)
+
+
+def test_check_idx(torch):
+    good = dev(np.array([0, 3, 9], np.int32))
+    assert int(jano.check_idx(good, 10).item()) == 0
+    for bad in ([0, 3, 3], [0, 10], [-1, 2], [5, 2]):
+        assert int(jano.check_idx(dev(np.array(bad, np.int32)), 10).item()) == jano.JANO_E_RANGE
+
+
+# ----------------------------------------------------------------- attention
+
+def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0):
+    Qb, Kb, Vb = synth.qkv_bits(cfg, extra=extra)
+    if q_mult != 1.0:
+        Qb = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(Qb) * np.float32(q_mult))
+    rng = np.random.default_rng(11 + extra)
+    # the cache holds stale rows where the active tokens are; attn_step
+    # refreshes them from K_new / V_new = the current K / V rows
+    Kst, Vst = Kb.copy(), Vb.copy()
+    Kst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
+    Vst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
+    Kc, Vc = dev_bf16(Kst), dev_bf16(Vst)
+    out = jano.attn_step(dev_bf16(Qb[idx]), dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(Kc), Kb)
+    np.testing.assert_array_equal(host_bits(Vc), Vb)
+    got = host_bf16_f64(out)
+    rows = np.arange(len(idx)) if sample is None else sample
+    ref, _, _ = O.attn_step(Qb[idx], Kb[idx], Vb[idx], idx, Kst, Vst, queries=rows)
+    return got[rows], ref
+
+
+@pytest.mark.parametrize("cfg,frac", [(configs.TINY, 0.3), (configs.IMAGE, 0.3), (configs.IMAGE, 1.0)],
+                         ids=["tiny-30", "image-30", "image-100"])
+def test_attention_full_compare(torch, cfg, frac):
+    print("attention", cfg.name, frac, flush=True)
+    idx = _idx_for(cfg, frac)
+    got, ref = _attn_case(torch, cfg, idx)
+    assert_attn_close(got, ref, "%s %.0f%%" % (cfg.name, 100 * frac))
+
+
+@pytest.mark.parametrize("cfg,frac", [(configs.V480, 0.25), (configs.V720, 0.25), (configs.V720, 0.10)],
+                         ids=["480p-25", "720p-25", "720p-10"])
+def test_attention_full_size_sampled(torch, cfg, frac):
+    print("attention sampled", cfg.name, frac, flush=True)
+    idx = _idx_for(cfg, frac)
+    rng = np.random.default_rng(17)
+    n = len(idx)
+    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, 192), replace=False)]))
+    got, ref = _attn_case(torch, cfg, idx, sample=sample)
+    assert_attn_close(got, ref, "%s %.0f%% sampled" % (cfg.name, 100 * frac))
+
+
+def test_full_activation_equals_dense(torch):
+    cfg = configs.IMAGE
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    Q, K, V = dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb)
+    dense = jano.attention(Q, K, V)
+    idx = np.arange(cfg.N, dtype=np.int32)
+    Kc, Vc = torch.zeros_like(K), torch.zeros_like(V)
+    step = jano.attn_step(Q, K, V, dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    # same kernel, same inputs after the scatter: identical bits
+    np.testing.assert_array_equal(host_bits(step), host_bits(dense))
+
+
+def test_cached_equals_recompute(torch):
+    # frozen rows current in the cache, active rows refreshed -> the active
+    # queries' outputs equal dense attention's rows
+    cfg = configs.IMAGE
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    idx = _idx_for(cfg, 0.3)
+    dense = host_bits(jano.attention(dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb)))
+    Kst, Vst = Kb.copy(), Vb.copy()
+    Kst[idx] = 0
+    Vst[idx] = 0
+    Kc, Vc = dev_bf16(Kst), dev_bf16(Vst)
+    step = jano.attn_step(dev_bf16(Qb[idx]), dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(step), dense[idx])
+
+
+@pytest.mark.parametrize("n,N,d", [(1, 1, 64), (31, 100, 64), (129, 65, 128), (200, 1000, 128),
+                                   (64, 129, 64), (257, 4097, 128)])
+def test_attention_ragged(torch, n, N, d):
+    print("attention ragged", n, N, d, flush=True)
+    rng = np.random.default_rng(n * 7 + N)
+    H = 3
+    Q = synth.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
+    K = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    V = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    out = jano.attention(dev_bf16(Q), dev_bf16(K), dev_bf16(V))
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Q), O.bf16_to_f64(K), O.bf16_to_f64(V))
+    assert_attn_close(host_bf16_f64(out), ref, "ragged n=%d N=%d d=%d" % (n, N, d))
+
+
+def test_attention_peaked_and_scale(torch):
+    # large logits exercise the running-max rescale; an explicit scale is used
+    cfg = configs.IMAGE
+    idx = _idx_for(cfg, 0.3)
+    got, ref = _attn_case(torch, cfg, idx, q_mult=8.0, extra=1)
+    assert_attn_close(got, ref, "peaked")
+    rng = np.random.default_rng(2)
+    Q = synth.f32_to_bf16_bits(rng.standard_normal((70, 2, 64)).astype(np.float32))
+    K = synth.f32_to_bf16_bits(rng.standard_normal((300, 2, 64)).astype(np.float32))
+    V = synth.f32_to_bf16_bits(rng.standard_normal((300, 2, 64)).astype(np.float32))
+    out = jano.attention(dev_bf16(Q), dev_bf16(K), dev_bf16(V), scale=0.3)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Q), O.bf16_to_f64(K), O.bf16_to_f64(V), scale=0.3)
+    assert_attn_close(host_bf16_f64(out), ref, "scale=0.3")
+
+
+def test_attention_closed_forms(torch):
+    rng = np.random.default_rng(4)
+    n, N, H, d = 40, 300, 2, 128
+    V = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    K = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    Qz = np.zeros((n, H, d), np.uint16)
+    out = host_bf16_f64(jano.attention(dev_bf16(Qz), dev_bf16(K), dev_bf16(V)))
+    mean = O.bf16_to_f64(V).mean(axis=0)
+    assert np.abs(out - mean[None]).max() <= 2e-2 * max(1.0, np.abs(mean).max())
+    one = host_bf16_f64(jano.attention(dev_bf16(Qz), dev_bf16(K[:1]), dev_bf16(V[:1])))
+    np.testing.assert_array_equal(one, np.broadcast_to(O.bf16_to_f64(V[:1]), one.shape))

@@ -1,0 +1,178 @@
+// C ABI of libjano: host-side argument validation and kernel launches.
+// Every check happens before anything is enqueued, so a non-zero return
+// means nothing ran and no output was touched.
+#include <math.h>
+
+#include "../../include/jano.h"
+#include "kernels.hpp"
+
+using jano::AnalyzeGeom;
+
+namespace {
+
+constexpr int64_t kMaxRows = 0x7fffffffLL;
+
+bool grid_ok(const jano_grid *g, AnalyzeGeom *out) {
+  if (!g) return false;
+  return jano::analyze_plan(g->K, g->C, g->F, g->H, g->W, g->bF, g->bH, g->bW, g->pF, g->pH,
+                            g->pW, out);
+}
+
+bool sched_ok(const jano_sched *sc) {
+  if (!sc) return false;
+  if (sc->T < 1 || sc->W < 0 || sc->Cd < 0 || sc->W + sc->Cd > sc->T) return false;
+  for (int i = 0; i < 3; ++i)
+    if (sc->period[i] < 1) return false;
+  return true;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? JANO_OK : JANO_E_HIP; }
+
+void due_flags(const jano_sched *sc, int step, int due[3]) {
+  const bool dense = step < sc->W || step >= sc->T - sc->Cd;
+  for (int i = 0; i < 3; ++i) due[i] = dense || ((step - sc->W) % sc->period[i] == 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+int jano_abi_version(void) { return JANO_ABI_VERSION; }
+
+const char *jano_status_string(int status) {
+  switch (status) {
+    case JANO_OK: return "ok";
+    case JANO_E_INVAL: return "invalid argument";
+    case JANO_E_UNSUPPORTED: return "unsupported configuration";
+    case JANO_E_RANGE: return "index out of range or not strictly ascending";
+    case JANO_E_WORKSPACE: return "workspace missing or too small";
+    case JANO_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int jano_grid_sizes(const jano_grid *g, int64_t *num_blocks, int64_t *num_tokens) {
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a)) return JANO_E_INVAL;
+  if (num_blocks) *num_blocks = a.B;
+  if (num_tokens)
+    *num_tokens = static_cast<int64_t>(g->F / g->pF) * (g->H / g->pH) * (g->W / g->pW);
+  return JANO_OK;
+}
+
+int jano_schedule_count(const int32_t *counts, const jano_sched *sc, int step, int64_t *n_act) {
+  if (!counts || !n_act || !sched_ok(sc) || step < 0 || step >= sc->T) return JANO_E_INVAL;
+  int due[3];
+  due_flags(sc, step, due);
+  int64_t n = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (counts[i] < 0) return JANO_E_INVAL;
+    if (due[i]) n += counts[i];
+  }
+  *n_act = n;
+  return JANO_OK;
+}
+
+size_t jano_analyze_workspace_bytes(const jano_grid *g) {
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a)) return 0;
+  return jano::analyze_ws_bytes(a);
+}
+
+int jano_analyze(const float *lat, const jano_grid *g, int static_permille, int moderate_permille,
+                 float *scores, uint8_t *levels, int32_t *level_tok_counts, void *ws,
+                 size_t ws_bytes, void *stream) {
+  if (!lat || !scores || !levels || !level_tok_counts) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a)) return JANO_E_INVAL;
+  if (static_permille < 0 || moderate_permille < 0 || static_permille + moderate_permille > 1000)
+    return JANO_E_INVAL;
+  if (!ws || ws_bytes < jano::analyze_ws_bytes(a)) return JANO_E_WORKSPACE;
+  const long long B = a.B;
+  const int nS = static_cast<int>((static_permille * B + 500) / 1000);
+  const int nSM = static_cast<int>(((static_permille + moderate_permille) * B + 500) / 1000);
+  return hip_status(jano::launch_analyze(lat, a, nS, nSM, scores, levels, level_tok_counts, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *sc, int step,
+                  int32_t *idx, int32_t *n_act_dev, void *stream) {
+  if (!levels || !idx || !n_act_dev) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a) || !sched_ok(sc) || step < 0 || step >= sc->T) return JANO_E_INVAL;
+  jano::SchedGeom s{};
+  s.Ft = g->F / g->pF;
+  s.Ht = g->H / g->pH;
+  s.Wt = g->W / g->pW;
+  const int64_t N = static_cast<int64_t>(s.Ft) * s.Ht * s.Wt;
+  if (N > kMaxRows) return JANO_E_UNSUPPORTED;
+  s.N = static_cast<int>(N);
+  s.pF = g->pF; s.pH = g->pH; s.pW = g->pW;
+  s.bF = g->bF; s.bH = g->bH; s.bW = g->bW;
+  s.nBH = a.nBH;
+  s.nBW = a.nBW;
+  due_flags(sc, step, s.due);
+  return hip_status(jano::launch_schedule(levels, s, idx, n_act_dev, static_cast<hipStream_t>(stream)));
+}
+
+int jano_gather_rows(const uint16_t *X, int64_t N, int64_t D, const int32_t *idx, int64_t n_act,
+                     uint16_t *X_act, void *stream) {
+  if (N < 1 || D < 1 || n_act < 0 || n_act > kMaxRows || N > kMaxRows) return JANO_E_INVAL;
+  if (n_act == 0) return JANO_OK;
+  if (!X || !idx || !X_act) return JANO_E_INVAL;
+  return hip_status(jano::launch_gather_rows(X, D, idx, n_act, X_act, static_cast<hipStream_t>(stream)));
+}
+
+int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t *idx,
+                    int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int64_t HD,
+                    void *stream) {
+  if (N < 1 || HD < 1 || n_act < 0 || n_act > N || N > kMaxRows) return JANO_E_INVAL;
+  if (n_act == 0) return JANO_OK;
+  if (!K_new || !V_new || !idx || !Kc || !Vc) return JANO_E_INVAL;
+  return hip_status(jano::launch_scatter_kv(K_new, V_new, idx, n_act, Kc, Vc, HD,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
+                   int64_t N, int H, int d, float scale, uint16_t *out, void *stream) {
+  if (N < 1 || H < 1 || n_q < 0 || N > kMaxRows || n_q > kMaxRows || !(scale == scale))
+    return JANO_E_INVAL;
+  if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
+  if (n_q > 0 && (!Q || !out)) return JANO_E_INVAL;
+  if (!Kc || !Vc) return JANO_E_INVAL;
+  if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(out)) return JANO_E_INVAL;
+  if (H > 65535) return JANO_E_UNSUPPORTED;
+  if (n_q == 0) return JANO_OK;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
+  return hip_status(jano::launch_attention(Q, n_q, Kc, Vc, N, H, d, sc, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
+                   const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
+                   int d, float scale, uint16_t *out, void *stream) {
+  if (N < 1 || H < 1 || n_act < 0 || n_act > N || N > kMaxRows || !(scale == scale))
+    return JANO_E_INVAL;
+  if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
+  if (H > 65535) return JANO_E_UNSUPPORTED;
+  if (!Kc || !Vc) return JANO_E_INVAL;
+  if (n_act == 0) return JANO_OK;
+  if (!Q_act || !K_new || !V_new || !idx || !out) return JANO_E_INVAL;
+  if (!aligned16(Q_act) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(out)) return JANO_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t HD = static_cast<int64_t>(H) * d;
+  hipError_t e = jano::launch_scatter_kv(K_new, V_new, idx, n_act, Kc, Vc, HD, s);
+  if (e != hipSuccess) return JANO_E_HIP;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
+  return hip_status(jano::launch_attention(Q_act, n_act, Kc, Vc, N, H, d, sc, out, s));
+}
+
+int jano_check_idx(const int32_t *idx, int64_t n_act, int64_t N, int32_t *flag_dev, void *stream) {
+  if (!flag_dev || n_act < 0 || N < 1 || n_act > kMaxRows) return JANO_E_INVAL;
+  if (n_act > 0 && !idx) return JANO_E_INVAL;
+  return hip_status(jano::launch_check_idx(idx, n_act, N, flag_dev, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal launch interface between the C ABI (capi.hip) and the kernels.
+// All launchers assume arguments were validated by the caller and return a
+// hipError_t from the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jano {
+
+// Geometry of one analyzer launch, fully derived on the host.
+struct AnalyzeGeom {
+  int K, C, F, H, W;
+  int bF, bH, bW;
+  int pF, pH, pW;
+  int nBF, nBH, nBW;
+  int B;
+  int R;    // latent rows per strip (a strip is one wave's row range)
+  int G;    // strips per block row, bH / R
+  int CW;   // useful columns per wave (multiple of bW, < 64)
+  int nWC;  // column chunks, ceil(W / CW)
+  int FC;   // frames per chunk (multiple of bF)
+  int nFC;  // frame chunks, ceil(F / FC)
+  bool fast;  // streaming stencil kernel instantiated for (K, R)
+};
+
+bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int pF,
+                  int pH, int pW, AnalyzeGeom *g);
+size_t analyze_ws_bytes(const AnalyzeGeom &g);
+hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nSM,
+                          float *scores, uint8_t *levels, int32_t *counts, void *ws,
+                          hipStream_t s);
+
+struct SchedGeom {
+  int Ft, Ht, Wt;         // token grid
+  int pF, pH, pW;         // patch
+  int bF, bH, bW;         // block (latent px)
+  int nBH, nBW;           // block grid (H, W)
+  int N;
+  int due[3];             // whether level 1/2/3 is recomputed at this step
+};
+hipError_t launch_schedule(const uint8_t *levels, const SchedGeom &g, int32_t *idx,
+                           int32_t *n_act, hipStream_t s);
+hipError_t launch_check_idx(const int32_t *idx, int64_t n, int64_t N, int32_t *flag,
+                            hipStream_t s);
+
+hipError_t launch_gather_rows(const uint16_t *X, int64_t D, const int32_t *idx,
+                              int64_t n, uint16_t *out, hipStream_t s);
+hipError_t launch_scatter_kv(const uint16_t *Kn, const uint16_t *Vn, const int32_t *idx,
+                             int64_t n, uint16_t *Kc, uint16_t *Vc, int64_t HD,
+                             hipStream_t s);
+
+hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K,
+                            const uint16_t *V, int64_t N, int H, int d, float scale,
+                            uint16_t *out, hipStream_t s);
+
+}  // namespace jano

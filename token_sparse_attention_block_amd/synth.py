@@ -28,8 +28,11 @@ def rng(cfg_id: int, role: int, extra: int = 0) -> np.random.Generator:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bits."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding here expects finite inputs")
+    # finite inputs never carry past bit 31 here
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
@@ -103,12 +106,13 @@ def latents(cfg, signal: bool = False) -> np.ndarray:
     return out
 
 
-def qkv_bits(cfg, n_tokens: int | None = None, extra: int = 0):
-    """bf16 bit patterns (uint16) of Q, K, V, each [N, heads, d], N(0,1)*scale."""
+def qkv_bits(cfg, n_tokens: int | None = None, extra: int = 0, which: str = "qkv"):
+    """bf16 bit patterns (uint16) of Q, K, V, each [N, heads, d], N(0,1)*scale.
+    `which` selects a subset (e.g. "q"); each tensor has its own seed."""
     N = cfg.N if n_tokens is None else n_tokens
     shape = (N, cfg.heads, cfg.d)
     out = []
-    for role in (ROLE_Q, ROLE_K, ROLE_V):
+    for role in [{"q": ROLE_Q, "k": ROLE_K, "v": ROLE_V}[c] for c in which]:
         x = rng(cfg.cfg_id, role, extra).standard_normal(shape, dtype=np.float32)
         out.append(f32_to_bf16_bits(x * np.float32(cfg.qkv_scale)))
     return tuple(out)
