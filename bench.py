@@ -1,0 +1,360 @@
+"""Bench of the Jano hot path on one MI355X.
+
+Workload (default): the 720p video-shaped grid, 21x45x80 = 75600 tokens,
+40 heads, d = 128, bf16; warm-up latents 5 x [16, 21, 90, 160] fp32.
+One step = one pass of the whole path on resident inputs:
+    jano_analyze (block scores + levels, 40/30/30 mix shifted so that the
+    Active level holds the configured share) -> jano_schedule at an
+    Active-only interleaved step -> jano_gather_rows (active rows of Q) ->
+    jano_scatter_kv (fresh K/V rows into the full-sequence cache) ->
+    jano_attention (active queries against the whole cache).
+`value` = active-query attention FLOPs per step (4 * n_act * N * H * d) divided
+by the measured wall time of the whole step. The dense reference (all N
+queries), the 10/25/50% step speedups and the 50-step interleaved run on the
+480p grid are reported beside it, as are per-kernel times from HIP events and
+the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--frac 0.25] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ACTIVE_ONLY_OFFSET = 1         # (step - W) odd: only Active tokens are due
+MIX_FOR_ACTIVE = {0.10: (600, 300), 0.25: (450, 300), 0.50: (300, 200), 1.0: (0, 0)}
+
+
+def _ev(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+def kernel_source_hash(name):
+    p = os.path.join(ROOT, "token_sparse_attention_block_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, only
+    if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(workload, {}).get(kernel_file)
+    if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+class Path:
+    """Device-resident inputs and outputs of one workload."""
+
+    def __init__(self, torch, jano, synth, cfg, frac, n_lat_copies=3):
+        self.torch, self.jano, self.cfg, self.frac = torch, jano, cfg, frac
+        dev = "cuda"
+        self.spec = jano.GridSpec.of(cfg)
+        lat = synth.latents(cfg)
+        # rotate several latent copies so the analyzer streams from HBM rather
+        # than from the 256 MB last-level cache
+        self.lats = [torch.from_numpy(lat).to(dev) for _ in range(n_lat_copies)]
+        self.spm, self.mpm = MIX_FOR_ACTIVE[frac]
+        B, N = jano.grid_sizes(self.spec)
+        self.B, self.N = B, N
+        self.scores = torch.empty(B, dtype=torch.float32, device=dev)
+        self.levels = torch.empty(B, dtype=torch.uint8, device=dev)
+        self.counts = torch.empty(3, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(jano.analyze_workspace_bytes(self.spec), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(N, dtype=torch.int32, device=dev)
+        self.n_dev = torch.empty(1, dtype=torch.int32, device=dev)
+        sc = cfg.schedule
+        self.sched = (sc.T, sc.W, sc.Cd, sc.periods)
+        self.step_id = sc.W + ACTIVE_ONLY_OFFSET if frac < 1.0 else 0
+        # the one host sync of a generation: level token counts -> n_act
+        self.analyze(0)
+        torch.cuda.synchronize()
+        self.n_act = jano.schedule_count(self.counts.cpu().tolist(), sc.T, sc.W, sc.Cd,
+                                         sc.periods, self.step_id)
+
+    def analyze(self, i):
+        self.jano.analyze(self.lats[i % len(self.lats)], self.spec, self.spm, self.mpm,
+                          self.scores, self.levels, self.counts, self.ws)
+
+    def schedule(self):
+        T, W, Cd, per = self.sched
+        self.jano.schedule(self.levels, self.spec, self.step_id, T, W, Cd, per, self.idx, self.n_dev)
+
+
+def upload_bf16(torch, bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def make_qkv(torch, synth, cfg):
+    return [upload_bf16(torch, b) for b in synth.qkv_bits(cfg)]
+
+
+def run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, ev=None):
+    """One whole pass; `ev` (list of 6 events) brackets each kernel."""
+    jano = p.jano
+    if ev:
+        ev[0].record()
+    p.analyze(i)
+    if ev:
+        ev[1].record()
+    p.schedule()
+    if ev:
+        ev[2].record()
+    idx = p.idx[:p.n_act]
+    jano.gather_rows(Q, idx, p.n_act, out=q_act)
+    if ev:
+        ev[3].record()
+    jano.scatter_kv(Kn, Vn, idx, Kc, Vc, n_act=p.n_act)
+    if ev:
+        ev[4].record()
+    jano.attention(q_act, Kc, Vc, out=out, n_q=p.n_act)
+    if ev:
+        ev[5].record()
+
+
+def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup):
+    p = Path(torch, jano, synth, cfg, frac)
+    n = p.n_act
+    H, d = cfg.heads, cfg.d
+    idx = p.idx[:n]
+    p.schedule()
+    Kn = jano.gather_rows(K, idx, n)     # fresh rows, as a projection would emit them
+    Vn = jano.gather_rows(V, idx, n)
+    q_act = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    for i in range(warmup):
+        run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out)
+    torch.cuda.synchronize()
+    evs = [[_ev(torch) for _ in range(6)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    names = ("analyze", "schedule", "gather", "scatter", "attention")
+    per = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(names)}
+    return p, n, wall * 1e3, per
+
+
+def time_dense(torch, jano, Q, Kc, Vc, reps):
+    out = torch.empty_like(Q)
+    jano.attention(Q, Kc, Vc, out=out)
+    torch.cuda.synchronize()
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(reps):
+        jano.attention(Q, Kc, Vc, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def sched_run(torch, jano, synth, cfg):
+    """50-step interleaved run on the 480p grid: analyzer once after the
+    warm-up steps, then per step schedule -> gather -> scatter -> attention
+    (dense steps use all tokens); total versus 50 dense attention steps."""
+    dev = "cuda"
+    H, d, N = cfg.heads, cfg.d, cfg.N
+    sc = cfg.schedule
+    spec = jano.GridSpec.of(cfg)
+    lat = torch.from_numpy(synth.latents(cfg)).to(dev)
+    Q, K, V = make_qkv(torch, synth, cfg)
+    Kc, Vc = K.clone(), V.clone()
+    B, _ = jano.grid_sizes(spec)
+    idx = torch.empty(N, dtype=torch.int32, device=dev)
+    n_dev = torch.empty(1, dtype=torch.int32, device=dev)
+    q_act = torch.empty_like(Q)
+    out = torch.empty_like(Q)
+    scores, levels, counts = jano.analyze(lat, spec)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().tolist()
+    n_per = [jano.schedule_count(cnt, sc.T, sc.W, sc.Cd, sc.periods, s) for s in range(sc.T)]
+
+    def one_run(ev_a, ev_b):
+        ev_a.record()
+        jano.analyze(lat, spec, 400, 300, scores, levels, counts)
+        for s in range(sc.T):
+            n = n_per[s]
+            jano.schedule(levels, spec, s, sc.T, sc.W, sc.Cd, sc.periods, idx, n_dev)
+            ii = idx[:n]
+            jano.gather_rows(Q, ii, n, out=q_act[:n])
+            jano.scatter_kv(K, V, ii, Kc, Vc, n_act=n)   # stand-in fresh rows: same bytes
+            jano.attention(q_act, Kc, Vc, out=out, n_q=n)
+        ev_b.record()
+
+    a, b = _ev(torch), _ev(torch)
+    one_run(a, b)
+    torch.cuda.synchronize()
+    a, b = _ev(torch), _ev(torch)
+    one_run(a, b)
+    torch.cuda.synchronize()
+    total = a.elapsed_time(b)
+    dense = time_dense(torch, jano, Q, Kc, Vc, 3)
+    return {"workload": "480p-32760tok-12h-d128-50steps", "n_act_per_step": n_per,
+            "total_ms": round(total, 3), "dense_50_steps_ms": round(50 * dense, 3),
+            "speedup": round(50 * dense / total, 4), "ideal_attention_speedup": round(50 * N / sum(n_per), 4)}
+
+
+def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    attention of a sample of active queries (all heads) against the full
+    75.6k-token cache, fp64 NumPy."""
+    from oracle import jano_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    N, H, d = cfg.N, cfg.heads, cfg.d
+    n_s = 64
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(N, size=n_s, replace=False))
+    Kf, Vf = O.bf16_to_f64(Kb), O.bf16_to_f64(Vb)
+    t0 = time.perf_counter()
+    O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
+    t = time.perf_counter() - t0
+    if t < seconds_hint / 3:   # grow the sample to roughly the time hint
+        n_s = int(min(N, n_s * max(1.0, seconds_hint / max(t, 1e-3))))
+        rows = np.sort(rng.choice(N, size=n_s, replace=False))
+        t0 = time.perf_counter()
+        O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
+        t = time.perf_counter() - t0
+    flops = 4.0 * n_s * N * H * d
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": "%d active queries x %d heads against the full %d-token K/V cache "
+                      "(fp64 NumPy attention; analyzer/schedule/gather/scatter excluded)" % (n_s, H, N)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--frac", type=float, default=0.25)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline fraction only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange inside the path)", file=sys.stderr)
+        sys.exit(2)
+    if args.frac not in MIX_FOR_ACTIVE:
+        sys.exit("--frac must be one of %s" % sorted(MIX_FOR_ACTIVE))
+
+    import torch
+    from token_sparse_attention_block_amd import configs, jano, synth
+    jano.lib()
+    torch.cuda.set_device(0)
+    cfg = configs.V720
+    N, H, d = cfg.N, cfg.heads, cfg.d
+    print("bench: generating %s inputs" % cfg.name, file=sys.stderr, flush=True)
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    Q, K, V = (upload_bf16(torch, b) for b in (Qb, Kb, Vb))
+    if args.no_cpu:
+        del Qb, Kb, Vb
+    Kc, Vc = K.clone(), V.clone()
+
+    print("bench: headline fraction %.2f" % args.frac, file=sys.stderr, flush=True)
+    p, n_act, ms_step, per = time_fraction(torch, jano, synth, cfg, args.frac, Q, K, V, Kc, Vc,
+                                           args.steps, args.warmup)
+    attn_flops = 4.0 * n_act * N * H * d
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    achieved = attn_flops / (per["attention"] * 1e-3) / 1e12
+    lat_bytes = cfg.latent_bytes + p.B * 5 + 12
+    row_bytes = H * d * 2
+    kernels = {
+        "analyze": {"ms": per["analyze"], "bytes": lat_bytes,
+                    "GB/s": lat_bytes / (per["analyze"] * 1e-3) / 1e9},
+        "schedule": {"ms": per["schedule"]},
+        "gather": {"ms": per["gather"], "bytes": 2 * n_act * row_bytes,
+                   "GB/s": 2 * n_act * row_bytes / (per["gather"] * 1e-3) / 1e9},
+        "scatter": {"ms": per["scatter"], "bytes": 4 * n_act * row_bytes,
+                    "GB/s": 4 * n_act * row_bytes / (per["scatter"] * 1e-3) / 1e9},
+        "attention": {"ms": per["attention"], "flops": attn_flops, "TFLOP/s": achieved},
+    }
+    for k in ("analyze", "gather", "scatter"):
+        kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
+    kernels["attention"]["frac_mfma"] = achieved / PEAK_BF16_TFLOPS
+    for v in kernels.values():
+        for kk in list(v):
+            if isinstance(v[kk], float):
+                v[kk] = round(v[kk], 5)
+
+    print("bench: dense reference", file=sys.stderr, flush=True)
+    dense_ms = time_dense(torch, jano, Q, Kc, Vc, 3)
+    dense_tflops = 4.0 * N * N * H * d / (dense_ms * 1e-3) / 1e12
+    speedups = {}
+    path_ms_head = per["gather"] + per["scatter"] + per["attention"]
+    speedups["%d%%" % round(100 * args.frac)] = {
+        "n_act": n_act, "path_ms": round(path_ms_head, 4), "speedup": round(dense_ms / path_ms_head, 4),
+        "attention_TFLOP/s": round(achieved, 2)}
+    extra = {}
+    if not args.no_extra:
+        for f in (0.10, 0.25, 0.50):
+            if abs(f - args.frac) < 1e-9:
+                continue
+            print("bench: fraction %.2f" % f, file=sys.stderr, flush=True)
+            pf, nf, _, perf = time_fraction(torch, jano, synth, cfg, f, Q, K, V, Kc, Vc, 3, 1)
+            pm = perf["gather"] + perf["scatter"] + perf["attention"]
+            speedups["%d%%" % round(100 * f)] = {
+                "n_act": nf, "path_ms": round(pm, 4), "speedup": round(dense_ms / pm, 4),
+                "attention_TFLOP/s": round(4.0 * nf * N * H * d / (perf["attention"] * 1e-3) / 1e12, 2)}
+            del pf
+        del Q, K, V, Kc, Vc
+        torch.cuda.empty_cache()
+        print("bench: 50-step interleaved run (480p)", file=sys.stderr, flush=True)
+        extra["sched480p"] = sched_run(torch, jano, synth, configs.SCHED480)
+
+    cpu = None
+    if not args.no_cpu:
+        print("bench: CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, Qb, Kb, Vb)
+
+    line = {
+        "metric": "active-query attention TFLOP/s + step speedup vs dense at 75.6k tokens",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V; x_t=(1-t)x0+t*eps warm-up latents)",
+        "config": {"workload": "720p-75600tok-40h-d128-active%d" % round(100 * args.frac),
+                   "tokens": N, "heads": H, "head_dim": d, "n_act": n_act,
+                   "latents": list(cfg.latent_shape), "block_latent_px": list(cfg.block),
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
+                     "traffic": load_traffic("attention.hip", "720p-active%d" % round(100 * args.frac)),
+                     "kernel": "attn_fwd_kernel<128>"},
+        "cpu_baseline": cpu,
+        "step_speedup_vs_dense": speedups,
+        "dense": {"ms": round(dense_ms, 4), "TFLOP/s": round(dense_tflops, 3)},
+        "kernels": kernels,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -89,8 +89,12 @@ __global__ __launch_bounds__(kAnalyzeWaves * kWave) void analyze_stream_kernel(
 
   const size_t plane = static_cast<size_t>(g.H) * g.W;
   const size_t kstride = static_cast<size_t>(g.C) * g.F * plane;
-  const float *base = lat + static_cast<size_t>(c) * g.F * plane +
-                      static_cast<size_t>(max(h0, 0)) * g.W + (col_ok ? w : 0);
+  // Loads are unconditional from clamped (always in-bounds) addresses and
+  // masked afterwards, so all (R+1)*K loads of a frame are in flight at once.
+  const float *base = lat + static_cast<size_t>(c) * g.F * plane + min(w, g.W - 1);
+  int rowoff[R + 1];
+#pragma unroll
+  for (int r = 0; r <= R; ++r) rowoff[r] = min(h0 + r, g.H - 1) * g.W;
 
   double Dprev[KD][R];
 #pragma unroll
@@ -103,12 +107,14 @@ __global__ __launch_bounds__(kAnalyzeWaves * kWave) void analyze_stream_kernel(
     const float *p = base + static_cast<size_t>(f) * plane;
     float x[KT][R + 1];
 #pragma unroll
+    for (int r = 0; r <= R; ++r)
+#pragma unroll
+      for (int k = 0; k < KT; ++k) x[k][r] = p[k * kstride + rowoff[r]];
+#pragma unroll
     for (int r = 0; r <= R; ++r) {
       const bool ok = col_ok && r < rows_loaded;
 #pragma unroll
-      for (int k = 0; k < KT; ++k)
-        x[k][r] = ok ? __builtin_nontemporal_load(p + k * kstride + static_cast<size_t>(r) * g.W)
-                     : 0.0f;
+      for (int k = 0; k < KT; ++k) x[k][r] = ok ? x[k][r] : 0.0f;
     }
     double D[KD][R + 1];
 #pragma unroll
@@ -193,11 +199,16 @@ __device__ __forceinline__ int axis_tokens(int j, int per_block, int ntok) {
 
 // Finds, for each of two target ranks, the 64-bit key (score bits, block id)
 // at that rank. keys[] holds the fp32 score bits (non-negative scores are
-// ordered like their bit patterns).
-__device__ void select_two(const uint32_t *keys, int B, const int target[2],
-                           uint64_t thr[2], uint32_t (*hist)[256], uint32_t *sh) {
+// ordered like their bit patterns). Radix select, 8 bits per pass: build the
+// digit histogram of the candidates in LDS, then 512 threads scan the two
+// 256-bin histograms in parallel to find the digit holding each target.
+__device__ void select_two(const uint32_t *keys, int B, const int target[2], uint64_t thr[2],
+                           uint32_t (*hist)[256], uint32_t *sh) {
   const int tid = threadIdx.x;
-  // sh[0..1] prefix, sh[2..3] remaining rank, sh[4..5] found id, sh[6..] scratch
+  const int lane = tid % kWave, wv = tid / kWave, nw = blockDim.x / kWave;
+  // sh[0..1] prefix, sh[2..3] remaining rank, sh[4..5] found id,
+  // sh[8..8+2*nw) per-wave scratch
+  uint32_t *wtot = sh + 8;
   if (tid < 2) {
     sh[tid] = 0u;
     sh[2 + tid] = static_cast<uint32_t>(target[tid]);
@@ -215,22 +226,31 @@ __device__ void select_two(const uint32_t *keys, int B, const int target[2],
       if ((u & mask) == p1) atomicAdd(&hist[1][dgt], 1u);
     }
     __syncthreads();
-    if (tid < 2) {
-      uint32_t k = sh[2 + tid], cum = 0u;
-      int d = 0;
-      for (; d < 255; ++d) {
-        if (cum + hist[tid][d] > k) break;
-        cum += hist[tid][d];
+    // threads 0..511: target t = tid / 256, bin = tid % 256 (4 waves per target)
+    uint32_t h = 0, incl = 0;
+    if (tid < 512) {
+      h = hist[tid / 256][tid % 256];
+      incl = wave_inclusive_scan(h);
+      if (lane == kWave - 1) wtot[wv] = incl;
+    }
+    __syncthreads();
+    if (tid < 512) {
+      const int t = tid / 256;
+      uint32_t before = 0;
+      for (int j = t * 4; j < wv; ++j) before += wtot[j];
+      const uint32_t excl = before + incl - h;
+      const uint32_t k = sh[2 + t];
+      if (h > 0 && excl <= k && k < excl + h) {
+        sh[t] |= static_cast<uint32_t>(tid % 256) << shift;
+        sh[6 + t] = k - excl;
       }
-      sh[tid] |= static_cast<uint32_t>(d) << shift;
-      sh[2 + tid] = k - cum;
     }
     mask |= 255u << shift;
     __syncthreads();
+    if (tid < 2) sh[2 + tid] = sh[6 + tid];
+    __syncthreads();
   }
   // the target is the k-th (in id order) block whose bits equal the prefix
-  const int lane = tid % kWave, wv = tid / kWave, nw = blockDim.x / kWave;
-  uint32_t *wcnt = sh + 8;  // [2][nw]
   if (tid < 2) sh[4 + tid] = 0xFFFFFFFFu;
   uint32_t run0 = 0, run1 = 0;
   for (int b0 = 0; b0 < B; b0 += blockDim.x) {
@@ -241,18 +261,18 @@ __device__ void select_two(const uint32_t *keys, int B, const int target[2],
     const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
     __syncthreads();
     if (lane == 0) {
-      wcnt[wv] = __popcll(m0);
-      wcnt[nw + wv] = __popcll(m1);
+      wtot[wv] = __popcll(m0);
+      wtot[nw + wv] = __popcll(m1);
     }
     __syncthreads();
     uint32_t before0 = run0, before1 = run1, tot0 = 0, tot1 = 0;
     for (int j = 0; j < nw; ++j) {
       if (j < wv) {
-        before0 += wcnt[j];
-        before1 += wcnt[nw + j];
+        before0 += wtot[j];
+        before1 += wtot[nw + j];
       }
-      tot0 += wcnt[j];
-      tot1 += wcnt[nw + j];
+      tot0 += wtot[j];
+      tot1 += wtot[nw + j];
     }
     if (e0 && before0 + lanes_below(m0) == sh[2]) sh[4] = static_cast<uint32_t>(b);
     if (e1 && before1 + lanes_below(m1) == sh[3]) sh[5] = static_cast<uint32_t>(b);

@@ -213,6 +213,246 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t *__re
   }
 }
 
+// ---------------------------------------------------------------------------
+// d = 128 kernel: 8 waves x 32 queries, K/V tiles of 64 keys brought from
+// global memory straight into LDS (global_load_lds_dwordx4, no registers),
+// three LDS stages so two tiles are in flight while one is computed.
+//
+// LDS rows are 256 bytes (128 bf16) split in 16 chunks of 16 bytes; chunk c of
+// row r is stored at slot c ^ swz(r):
+//   K: swz(r) = r & 15 -- the S MFMA reads one chunk of 16 consecutive rows
+//      per 16 lanes (ds_read_b128), which then hit 16 different bank groups;
+//   V: swz(r) = 4*(r & 3) ^ ((r >> 2) & 3) -- the transposing reads
+//      (ds_read_b64_tr_b16) touch 4 consecutive rows x 4 chunks per half wave,
+//      which this maps onto 16 different bank groups.
+// The swizzle is applied on the global side: the lane that fills LDS slot s
+// fetches the chunk that belongs there.
+//
+// ds_read_b64_tr_b16 (per 16-lane group): lane j receives element (j % 4) of
+// the 4-element row that source lane 4e + j/4 addressed, for e = 0..3. When
+// source lane i addresses V[k0 + i/4][d0 + 4*(i%4) .. +3], lane j receives
+// V[k0 .. k0+3][d0 + j]: one dim, four consecutive keys -- the V^T operand of
+// the PV MFMA, read from row-major V.
+// ---------------------------------------------------------------------------
+constexpr int kW2 = 8;                      // waves per workgroup
+constexpr int kBM2 = kW2 * kQW;             // 256 queries per workgroup
+constexpr int kStages = 3;
+constexpr int kRowB = 256;                  // bytes per K/V row (d = 128)
+constexpr int kTileB = kBN * kRowB;         // 16 KB per K or V tile
+constexpr float kRescaleSlack = 8.0f;       // log2 headroom before rescaling
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt high bits [15:14]); expcnt and lgkmcnt at their "no wait" maximum.
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kWaitVmcnt4 = 0x0F74;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
+
+// One global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16*i. Issued from asm so that the compiler does not treat every
+// later LDS read as dependent on it (it would wait for all copies in flight,
+// including the tiles being prefetched); the kernel waits on vmcnt itself.
+// The instruction has no register results, only address operands.
+__device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  const uint32_t a = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
+  return __builtin_amdgcn_readfirstlane(a);
+}
+
+// Each wave fills 4 KB of a stage: 2 x 1 KB of K rows and 2 x 1 KB of V rows.
+__device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *Vh, size_t rs,
+                                           int N, int key0, char *stage_k, char *stage_v,
+                                           int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + lane / 16;    // tile row filled by this lane
+    const int slot = lane % 16;
+    const int key = min(key0 + r, N - 1);            // past-the-end rows: finite stand-ins
+    const uint16_t *krow = Kh + static_cast<size_t>(key) * rs;
+    const uint16_t *vrow = Vh + static_cast<size_t>(key) * rs;
+    char *kd = stage_k + (4 * (2 * wave + i)) * kRowB;
+    char *vd = stage_v + (4 * (2 * wave + i)) * kRowB;
+    copy16_to_lds(krow + 8 * (slot ^ swz_k(r)), lds_addr(kd));
+    copy16_to_lds(vrow + 8 * (slot ^ swz_v(r)), lds_addr(vd));
+  }
+}
+
+__global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int grp = lane / 16, gi = lane % 16;
+  const int head = blockIdx.y;
+  const size_t rs = static_cast<size_t>(H) * D;
+  const uint16_t *Kh = K + static_cast<size_t>(head) * D;
+  const uint16_t *Vh = V + static_cast<size_t>(head) * D;
+  const int ntiles = (N + kBN - 1) / kBN;
+
+  // start the first two tiles before anything else
+  issue_tile(Kh, Vh, rs, N, 0, lds[0][0], lds[0][1], wave, lane);
+  if (ntiles > 1) issue_tile(Kh, Vh, rs, N, kBN, lds[1][0], lds[1][1], wave, lane);
+
+  const int qrow = blockIdx.x * kBM2 + wave * kQW + l32;
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t *qp = Q + static_cast<size_t>(min(qrow, nq - 1)) * rs +
+                         static_cast<size_t>(head) * D + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      qf[t] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qp + 16 * t)));
+    // Consume the Q fragments here, so the compiler completes their loads
+    // before the key loop instead of leaving vmcnt waits inside it (where
+    // vmcnt counts the tile copies).
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) asm volatile("" : : "v"(qf[t]));
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // per-lane LDS byte offsets that do not depend on the tile
+  int koff[kBN / 32][D / 16];
+#pragma unroll
+  for (int mb = 0; mb < kBN / 32; ++mb)
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int r = mb * 32 + l32;
+      koff[mb][t] = r * kRowB + (((2 * t + hf) ^ swz_k(r)) * 16);
+    }
+  // V^T reads: key k0 + gi/4 with k0 = 16t + 4*(grp/2) (+8 for the second
+  // half), dims 32*db + 16*(grp%2) + 4*(gi%4) .. +3
+  int voff[kBN / 16][2];
+#pragma unroll
+  for (int t = 0; t < kBN / 16; ++t)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int key = 16 * t + 8 * h2 + 4 * (grp / 2) + gi / 4;
+      voff[t][h2] = key * kRowB + 8 * (gi % 2);
+    }
+  const int vchunk = 2 * (grp % 2) + (gi % 4) / 2;   // chunk within a 32-dim block
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j % kStages;
+    // This wave's loads of tile j are complete once at most the 4 loads of
+    // tile j+1 are outstanding; the barrier then makes every wave's part of
+    // tile j visible and guarantees stage (j+2)%3 (read in iteration j-1) is
+    // no longer in use.
+    if (j + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_barrier();
+    if (j + 2 < ntiles) {
+      const int s2 = (j + 2) % kStages;
+      issue_tile(Kh, Vh, rs, N, (j + 2) * kBN, lds[s2][0], lds[s2][1], wave, lane);
+    }
+    const char *kb = lds[st][0];
+    const char *vb = lds[st][1];
+
+    f32x16 s[kBN / 32];
+#pragma unroll
+    for (int mb = 0; mb < kBN / 32; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + koff[mb][t]);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[t], s[mb], 0, 0, 0);
+      }
+    }
+    if ((j + 1) * kBN > N) {
+#pragma unroll
+      for (int mb = 0; mb < kBN / 32; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * kBN + mb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+          if (key >= N) s[mb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < kBN / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scale_log2;
+    // lazy rescale: keep the running max unless it grew by more than the slack
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+#pragma unroll
+    for (int mb = 0; mb < kBN / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m_run));
+        s[mb][r] = p;
+        l_run += p;
+      }
+
+#pragma unroll
+    for (int t = 0; t < kBN / 16; ++t) {
+      const f32x16 &sv = s[t / 2];
+      const int r0 = 8 * (t % 2);
+      const f32x8 pf = {sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3],
+                        sv[r0 + 4], sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]};
+      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        bf16x4 part[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int key = 16 * t + 8 * h2 + 4 * (grp / 2) + gi / 4;
+          const int off = voff[t][h2] + (((4 * db + vchunk) ^ swz_v(key)) * 16);
+          part[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vb + off));
+        }
+        const bf16x8 a = {part[0][0], part[0][1], part[0][2], part[0][3],
+                          part[1][0], part[1][1], part[1][2], part[1][3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = l_run + shfl_xor_f32(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (qrow < nq) {
+    uint16_t *op = out + static_cast<size_t>(qrow) * rs + static_cast<size_t>(head) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
+                         o[db][4 * g4 + 3] * inv};
+        const bf16x4 b = __builtin_convertvector(v, bf16x4);
+        *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * g4 + 4 * hf) = b;
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, const uint16_t *V,
@@ -220,10 +460,11 @@ hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, co
   if (nq == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(static_cast<unsigned>((nq + kBM - 1) / kBM), static_cast<unsigned>(H));
-  if (d == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(kThreads), 0, s, Q, K, V, out,
+  if (d == 128) {
+    const dim3 grid2(static_cast<unsigned>((nq + kBM2 - 1) / kBM2), static_cast<unsigned>(H));
+    hipLaunchKernelGGL(attn_fwd_d128_kernel, grid2, dim3(kW2 * kWave), 0, s, Q, K, V, out,
                        static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
-  else
+  } else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, Q, K, V, out,
                        static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
   return hipGetLastError();

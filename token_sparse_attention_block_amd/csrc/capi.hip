@@ -111,6 +111,7 @@ int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *s
   s.N = static_cast<int>(N);
   s.pF = g->pF; s.pH = g->pH; s.pW = g->pW;
   s.bF = g->bF; s.bH = g->bH; s.bW = g->bW;
+  s.nBF = a.nBF;
   s.nBH = a.nBH;
   s.nBW = a.nBW;
   due_flags(sc, step, s.due);

@@ -34,4 +34,15 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t u = __shfl_up(v, off, kWave);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
 }  // namespace jano

@@ -36,7 +36,7 @@ struct SchedGeom {
   int Ft, Ht, Wt;         // token grid
   int pF, pH, pW;         // patch
   int bF, bH, bW;         // block (latent px)
-  int nBH, nBW;           // block grid (H, W)
+  int nBF, nBH, nBW;      // block grid
   int N;
   int due[3];             // whether level 1/2/3 is recomputed at this step
 };
