@@ -346,7 +346,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": load_traffic("attention.hip", "720p-active%d" % round(100 * args.frac)),
-                     "kernel": "attn_fwd_kernel<128>"},
+                     "kernel": "attn_fwd_d128_kernel"},
         "cpu_baseline": cpu,
         "step_speedup_vs_dense": speedups,
         "dense": {"ms": round(dense_ms, 4), "TFLOP/s": round(dense_tflops, 3)},
