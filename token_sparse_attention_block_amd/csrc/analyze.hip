@@ -25,10 +25,16 @@
 // written as one fp64 partial per (channel, strip, block): no atomics, so the
 // result is deterministic.
 //
-// Kernel 2 (levels_kernel, one workgroup) sums the partials in a fixed order,
-// divides by the closed-form term count, rounds the score to fp32, finds the
-// two level thresholds of the (score, block id) order by radix select, writes
-// the levels and counts tokens per level.
+// Kernel 2 (block_scores_kernel, one thread per block) sums the partials in a
+// fixed order, divides by the closed-form term count and rounds the score to
+// fp32; it also writes the block's token count. Kernel 3 (levels_kernel, one
+// workgroup) finds the two level thresholds of the (score, block id) order by
+// radix select, writes the levels and counts tokens per level.
+//
+// Grid mapping of kernel 1: workgroups are renumbered XCD-aware and waves are
+// ordered column chunk fastest, then strip, then frame chunk, so the waves
+// that re-read each other's halo cache lines run on one XCD (one L2) at the
+// same time.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,9 +42,13 @@ namespace jano {
 namespace {
 
 constexpr int kAnalyzeWaves = 4;          // waves per workgroup of kernel 1
+constexpr int kXcds = 8;                  // accelerator dies (each with an L2) per GPU
 constexpr int kLevelsThreads = 1024;      // kernel 2 is one workgroup
 constexpr int kMaxBlocks = 16384;         // kernel 2 keeps all keys in LDS
-constexpr int kTargetWaves = 4096;        // enough waves to fill 256 CUs
+#ifndef JANO_ANALYZE_TARGET_WAVES
+#define JANO_ANALYZE_TARGET_WAVES 4096
+#endif
+constexpr int kTargetWaves = JANO_ANALYZE_TARGET_WAVES;  // waves wanted in the grid
 
 __device__ __forceinline__ void flush_block_sum(double acc, const AnalyzeGeom &g, int lane,
                                                 int w0, int c, int sg, int bf, int bh,
@@ -56,20 +66,122 @@ __device__ __forceinline__ void flush_block_sum(double acc, const AnalyzeGeom &g
   }
 }
 
+// Value held by lane + 1 (DPP wavefront shift, a plain VALU move). Lane 63
+// receives 0; it never owns a gradient term (a wave owns at most 63 columns).
+__device__ __forceinline__ double from_next_lane(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x130, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), 0x130, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+
+// One (K, R) strip of one wave, streamed over its frame chunk. FULL: all R+1
+// rows (R owned + the +h halo row) lie inside the latent, so no row needs a
+// predicate; otherwise rows past the bottom edge are excluded term by term.
+template <int KT, int R, bool FULL>
+__device__ __forceinline__ void stream_strip(__amdgpu_buffer_rsrc_t rsrc, const AnalyzeGeom &g,
+                                             const uint32_t (&lane_off)[R + 1], int c, int f0,
+                                             int f_last, int f_end, int rows_loaded,
+                                             int rows_owned, bool own, bool has_wn, int lane,
+                                             int w0, int sg, int bh, double *__restrict__ part) {
+  constexpr int KD = KT - 2;
+  const uint32_t plane_b = static_cast<uint32_t>(g.H) * g.W * 4u;
+  const uint32_t kstride_b = static_cast<uint32_t>(g.C) * g.F * plane_b;
+  const uint32_t cbase_b = static_cast<uint32_t>(c) * g.F * plane_b;
+
+  double acc = 0.0;
+
+  // The next frame's loads are issued before the current frame is computed,
+  // so memory latency overlaps the fp64 work. Frames alternate between two
+  // register sets (x, D), so nothing is copied from one frame to the next.
+  auto load_frame = [&](int f, float (&xn)[KT][R + 1]) {
+    const uint32_t fb = cbase_b + static_cast<uint32_t>(f) * plane_b;
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int r = 0; r <= R; ++r)
+        xn[k][r] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, lane_off[r], fb + k * kstride_b, 0));
+  };
+  // processes frame f held in x (D_prev: the previous frame's D), prefetching
+  // frame f+1 into xn and leaving this frame's D in D_cur
+  auto frame = [&](int f, float (&x)[KT][R + 1], float (&xn)[KT][R + 1],
+                   const double (&D_prev)[KD][R + 1], double (&D)[KD][R + 1]) {
+    if (f < f_end) load_frame(f + 1, xn);
+#pragma unroll
+    for (int k = 0; k < KD; ++k)
+#pragma unroll
+      for (int r = 0; r <= R; ++r)
+        D[k][r] = (static_cast<double>(x[k + 2][r]) - 2.0 * static_cast<double>(x[k + 1][r])) +
+                  static_cast<double>(x[k][r]);
+    if (f > f0) {
+      // temporal terms of frame f-1 (pairs f-1 -> f), booked to block of f-1
+      double t = 0.0;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+          if (FULL || r < rows_owned) t += fabs(D[k][r] - D_prev[k][r]);
+      if (own) acc += t;
+      const int bprev = (f - 1) / g.bF;
+      if (f > f_last || f / g.bF != bprev) {
+        flush_block_sum(acc, g, lane, w0, c, sg, bprev, bh, part);
+        acc = 0.0;
+      }
+    }
+    if (f <= f_last) {
+      double th = 0.0, tw = 0.0;   // +h terms, +w terms
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+          const double right = from_next_lane(D[k][r]);   // +w neighbour
+          if (FULL || r < rows_owned) tw += fabs(right - D[k][r]);
+          if (FULL || r + 1 < rows_loaded) th += fabs(D[k][r + 1] - D[k][r]);
+        }
+      }
+      if (own) acc += th;
+      if (has_wn) acc += tw;
+    }
+  };
+
+  float xa[KT][R + 1], xb[KT][R + 1];
+  double Da[KD][R + 1], Db[KD][R + 1];
+#pragma unroll
+  for (int k = 0; k < KD; ++k)
+#pragma unroll
+    for (int r = 0; r <= R; ++r) Db[k][r] = 0.0;
+  load_frame(f0, xa);
+  for (int f = f0; f <= f_end; f += 2) {
+    frame(f, xa, xb, Db, Da);
+    if (f + 1 > f_end) break;
+    frame(f + 1, xb, xa, Da, Db);
+  }
+  if (f_end == f_last) flush_block_sum(acc, g, lane, w0, c, sg, f_last / g.bF, bh, part);
+}
+
 template <int KT, int R>
 __global__ __launch_bounds__(kAnalyzeWaves * kWave) void analyze_stream_kernel(
     const float *__restrict__ lat, AnalyzeGeom g, double *__restrict__ part, int total_waves) {
-  constexpr int KD = KT - 2;  // number of second differences
-  const int wave = blockIdx.x * kAnalyzeWaves + (threadIdx.x / kWave);
+  // Workgroups are dispatched round-robin over the XCDs, each with its own
+  // L2. Renumber them so that consecutive logical workgroups -- which read
+  // each other's halo rows, columns and frames -- run on the same XCD.
+  const int nwg = gridDim.x, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int logical = xcd * (nwg / kXcds) + min(xcd, nwg % kXcds) + slot;
+  // wave index made provably uniform, so everything derived from it stays in
+  // scalar registers (buffer offsets must be scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(logical * kAnalyzeWaves + (threadIdx.x / kWave));
   if (wave >= total_waves) return;  // uniform per wave
   const int lane = threadIdx.x % kWave;
 
+  // column chunk fastest, then strip, then frame chunk, then channel
   const int nStrips = g.nBH * g.G;
   int q = wave;
-  const int strip = q % nStrips;
-  q /= nStrips;
   const int wc = q % g.nWC;
   q /= g.nWC;
+  const int strip = q % nStrips;
+  q /= nStrips;
   const int fc = q % g.nFC;
   const int c = q / g.nFC;
 
@@ -77,7 +189,6 @@ __global__ __launch_bounds__(kAnalyzeWaves * kWave) void analyze_stream_kernel(
   const int h0 = bh * g.bH + sg * R;
   const int w0 = wc * g.CW;
   const int w = w0 + lane;
-  const bool col_ok = lane <= g.CW && w < g.W;  // loads (includes the halo lane)
   const bool own = lane < g.CW && w < g.W;      // owns gradient terms
   const bool has_wn = own && (w + 1 < g.W);
   const int rows_loaded = min(R + 1, g.H - h0);  // may be <= 0 for empty strips
@@ -87,74 +198,24 @@ __global__ __launch_bounds__(kAnalyzeWaves * kWave) void analyze_stream_kernel(
   const int f_last = min(f0 + g.FC, g.F) - 1;   // last owned frame
   const int f_end = min(f0 + g.FC, g.F - 1);    // last loaded frame (halo)
 
-  const size_t plane = static_cast<size_t>(g.H) * g.W;
-  const size_t kstride = static_cast<size_t>(g.C) * g.F * plane;
-  // Loads are unconditional from clamped (always in-bounds) addresses and
-  // masked afterwards, so all (R+1)*K loads of a frame are in flight at once.
-  const float *base = lat + static_cast<size_t>(c) * g.F * plane + min(w, g.W - 1);
-  int rowoff[R + 1];
+  // Loads go through a buffer resource (wave-uniform base, 32-bit offsets).
+  // Every load is issued unconditionally from a clamped in-bounds offset;
+  // clamped rows and columns hold real latent values and every term that
+  // would use them is excluded, so they need no masking.
+  const uint32_t bytes = static_cast<uint32_t>(static_cast<size_t>(g.K) * g.C * g.F * g.H * g.W * 4);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(lat), 0, bytes, 0x00020000);
+  uint32_t lane_off[R + 1];
 #pragma unroll
-  for (int r = 0; r <= R; ++r) rowoff[r] = min(h0 + r, g.H - 1) * g.W;
+  for (int r = 0; r <= R; ++r)
+    lane_off[r] = static_cast<uint32_t>(min(h0 + r, g.H - 1) * g.W + min(w, g.W - 1)) * 4u;
 
-  double Dprev[KD][R];
-#pragma unroll
-  for (int k = 0; k < KD; ++k)
-#pragma unroll
-    for (int r = 0; r < R; ++r) Dprev[k][r] = 0.0;
-  double acc = 0.0;
-
-  for (int f = f0; f <= f_end; ++f) {
-    const float *p = base + static_cast<size_t>(f) * plane;
-    float x[KT][R + 1];
-#pragma unroll
-    for (int r = 0; r <= R; ++r)
-#pragma unroll
-      for (int k = 0; k < KT; ++k) x[k][r] = p[k * kstride + rowoff[r]];
-#pragma unroll
-    for (int r = 0; r <= R; ++r) {
-      const bool ok = col_ok && r < rows_loaded;
-#pragma unroll
-      for (int k = 0; k < KT; ++k) x[k][r] = ok ? x[k][r] : 0.0f;
-    }
-    double D[KD][R + 1];
-#pragma unroll
-    for (int k = 0; k < KD; ++k)
-#pragma unroll
-      for (int r = 0; r <= R; ++r)
-        D[k][r] = (static_cast<double>(x[k + 2][r]) - 2.0 * static_cast<double>(x[k + 1][r])) +
-                  static_cast<double>(x[k][r]);
-
-    if (f > f0) {
-      // temporal terms of frame f-1 (pairs f-1 -> f), booked to block of f-1
-      double t = 0.0;
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int k = 0; k < KD; ++k)
-          if (r < rows_owned) t += fabs(D[k][r] - Dprev[k][r]);
-      if (own) acc += t;
-      const int bprev = (f - 1) / g.bF;
-      if (f > f_last || f / g.bF != bprev) {
-        flush_block_sum(acc, g, lane, w0, c, sg, bprev, bh, part);
-        acc = 0.0;
-      }
-    }
-    if (f <= f_last) {
-      double t = 0.0;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int k = 0; k < KD; ++k) {
-          const double right = shfl_down_f64(D[k][r], 1);   // +w neighbour
-          if (r < rows_owned && has_wn) t += fabs(right - D[k][r]);
-          if (r + 1 < rows_loaded) t += fabs(D[k][r + 1] - D[k][r]);  // +h
-          Dprev[k][r] = D[k][r];
-        }
-      }
-      if (own) acc += t;
-    }
-  }
-  if (f_end == f_last) flush_block_sum(acc, g, lane, w0, c, sg, f_last / g.bF, bh, part);
+  if (rows_loaded == R + 1)
+    stream_strip<KT, R, true>(rsrc, g, lane_off, c, f0, f_last, f_end, rows_loaded, rows_owned,
+                              own, has_wn, lane, w0, sg, bh, part);
+  else
+    stream_strip<KT, R, false>(rsrc, g, lane_off, c, f0, f_last, f_end, rows_loaded, rows_owned,
+                               own, has_wn, lane, w0, sg, bh, part);
 }
 
 // Slow path for shapes the streaming kernel does not cover (K > 8, odd block
@@ -219,11 +280,25 @@ __device__ void select_two(const uint32_t *keys, int B, const int target[2], uin
     for (int i = tid; i < 2 * 256; i += blockDim.x) hist[i / 256][i % 256] = 0u;
     __syncthreads();
     const uint32_t p0 = sh[0], p1 = sh[1];
-    for (int b = tid; b < B; b += blockDim.x) {
-      const uint32_t u = keys[b];
+    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
+      const int b = b0 + tid;
+      const uint32_t u = b < B ? keys[b] : 0u;
       const uint32_t dgt = (u >> shift) & 255u;
-      if ((u & mask) == p0) atomicAdd(&hist[0][dgt], 1u);
-      if ((u & mask) == p1) atomicAdd(&hist[1][dgt], 1u);
+      // Scores cluster, so most candidates of a wave share one digit: the
+      // first candidate's digit is counted with one atomic for the whole
+      // wave, the others one by one.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool cand = b < B && (u & mask) == (t == 0 ? p0 : p1);
+        const uint64_t cm = __ballot(cand);
+        if (cm) {
+          const int first = __ffsll(static_cast<long long>(cm)) - 1;
+          const uint32_t lead = __shfl(dgt, first, kWave);
+          const uint64_t same = __ballot(cand && dgt == lead);
+          if (lane == first) atomicAdd(&hist[t][lead], static_cast<uint32_t>(__popcll(same)));
+          if (cand && dgt != lead) atomicAdd(&hist[t][dgt], 1u);
+        }
+      }
     }
     __syncthreads();
     // threads 0..511: target t = tid / 256, bin = tid % 256 (4 waves per target)
@@ -250,8 +325,24 @@ __device__ void select_two(const uint32_t *keys, int B, const int target[2], uin
     if (tid < 2) sh[2 + tid] = sh[6 + tid];
     __syncthreads();
   }
-  // the target is the k-th (in id order) block whose bits equal the prefix
+  // The target is the k-th (in id order) block whose bits equal the prefix.
+  // When that score is unique (the usual case) the block is found directly;
+  // otherwise an ordered scan over the block ids ranks the equal scores.
   if (tid < 2) sh[4 + tid] = 0xFFFFFFFFu;
+  __syncthreads();
+  bool unique = true;
+  for (int t = 0; t < 2; ++t) unique = unique && hist[t][sh[t] & 255u] == 1u;
+  if (unique) {
+    for (int b = tid; b < B; b += blockDim.x) {
+      if (keys[b] == sh[0]) sh[4] = static_cast<uint32_t>(b);
+      if (keys[b] == sh[1]) sh[5] = static_cast<uint32_t>(b);
+    }
+    __syncthreads();
+    for (int t = 0; t < 2; ++t)
+      thr[t] = (static_cast<uint64_t>(sh[t]) << 32) | static_cast<uint64_t>(sh[4 + t]);
+    __syncthreads();
+    return;
+  }
   uint32_t run0 = 0, run1 = 0;
   for (int b0 = 0; b0 < B; b0 += blockDim.x) {
     const int b = b0 + tid;
@@ -285,9 +376,46 @@ __device__ void select_two(const uint32_t *keys, int B, const int target[2], uin
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kLevelsThreads) void levels_kernel(const double *__restrict__ part,
-                                                                AnalyzeGeom g, int nS, int nSM,
-                                                                float *__restrict__ scores,
+// Kernel 2: per-block score (fixed-order sum of the partials over channels
+// and strips, divided by the closed-form term count, rounded to fp32) and
+// per-block token count. One thread per block.
+__global__ __launch_bounds__(256) void block_scores_kernel(const double *__restrict__ part,
+                                                           AnalyzeGeom g,
+                                                           float *__restrict__ scores,
+                                                           int32_t *__restrict__ tokcnt) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= g.B) return;
+  const int B = g.B, CG = g.C * g.G;
+  double t = 0.0;
+  constexpr int kJ = 16;   // loads in flight per thread; summed in j order
+  for (int j0 = 0; j0 < CG; j0 += kJ) {
+    double v[kJ];
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj)
+      v[jj] = j0 + jj < CG ? part[static_cast<size_t>(j0 + jj) * B + b] : 0.0;
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) t += v[jj];
+  }
+  const int bw = b % g.nBW, bh = (b / g.nBW) % g.nBH, bf = b / (g.nBW * g.nBH);
+  const int f0 = bf * g.bF, f1 = min(f0 + g.bF, g.F);
+  const int h0 = bh * g.bH, h1 = min(h0 + g.bH, g.H);
+  const int w0 = bw * g.bW, w1 = min(w0 + g.bW, g.W);
+  const long long ef = f1 - f0, eh = h1 - h0, ew = w1 - w0;
+  const long long pos = (g.F >= 2 ? axis_terms(f0, f1, g.F) * eh * ew : 0) +
+                        (g.H >= 2 ? axis_terms(h0, h1, g.H) * ef * ew : 0) +
+                        (g.W >= 2 ? axis_terms(w0, w1, g.W) * ef * eh : 0);
+  const long long n = pos * (g.K - 2) * g.C;
+  scores[b] = n > 0 ? static_cast<float>(t / static_cast<double>(n)) : 0.0f;
+  const int tpbF = g.bF / g.pF, tpbH = g.bH / g.pH, tpbW = g.bW / g.pW;
+  tokcnt[b] = axis_tokens(bf, tpbF, g.F / g.pF) * axis_tokens(bh, tpbH, g.H / g.pH) *
+              axis_tokens(bw, tpbW, g.W / g.pW);
+}
+
+// Kernel 3 (one workgroup): the two rank thresholds of the (score, block id)
+// order, the levels, and the token count of each level.
+__global__ __launch_bounds__(kLevelsThreads) void levels_kernel(const float *__restrict__ scores,
+                                                                const int32_t *__restrict__ tokcnt,
+                                                                int B, int nS, int nSM,
                                                                 uint8_t *__restrict__ levels,
                                                                 int32_t *__restrict__ counts) {
   __shared__ uint32_t keys[kMaxBlocks];
@@ -295,27 +423,8 @@ __global__ __launch_bounds__(kLevelsThreads) void levels_kernel(const double *__
   __shared__ uint32_t sh[8 + 2 * (kLevelsThreads / kWave)];
   __shared__ int tok[3];
   const int tid = threadIdx.x;
-  const int B = g.B, CG = g.C * g.G;
-  const int tpbF = g.bF / g.pF, tpbH = g.bH / g.pH, tpbW = g.bW / g.pW;
-  const int Ft = g.F / g.pF, Ht = g.H / g.pH, Wt = g.W / g.pW;
   if (tid < 3) tok[tid] = 0;
-
-  for (int b = tid; b < B; b += blockDim.x) {
-    double t = 0.0;
-    for (int j = 0; j < CG; ++j) t += part[static_cast<size_t>(j) * B + b];
-    const int bw = b % g.nBW, bh = (b / g.nBW) % g.nBH, bf = b / (g.nBW * g.nBH);
-    const int f0 = bf * g.bF, f1 = min(f0 + g.bF, g.F);
-    const int h0 = bh * g.bH, h1 = min(h0 + g.bH, g.H);
-    const int w0 = bw * g.bW, w1 = min(w0 + g.bW, g.W);
-    const long long ef = f1 - f0, eh = h1 - h0, ew = w1 - w0;
-    const long long pos = (g.F >= 2 ? axis_terms(f0, f1, g.F) * eh * ew : 0) +
-                          (g.H >= 2 ? axis_terms(h0, h1, g.H) * ef * ew : 0) +
-                          (g.W >= 2 ? axis_terms(w0, w1, g.W) * ef * eh : 0);
-    const long long n = pos * (g.K - 2) * g.C;
-    const float s = n > 0 ? static_cast<float>(t / static_cast<double>(n)) : 0.0f;
-    scores[b] = s;
-    keys[b] = __float_as_uint(s);
-  }
+  for (int b = tid; b < B; b += blockDim.x) keys[b] = __float_as_uint(scores[b]);
   __syncthreads();
 
   uint64_t thr[2];
@@ -324,16 +433,17 @@ __global__ __launch_bounds__(kLevelsThreads) void levels_kernel(const double *__
   if (nS >= B) thr[0] = ~0ull;
   if (nSM >= B) thr[1] = ~0ull;
 
-  int my[3] = {0, 0, 0};
+  uint32_t my[3] = {0, 0, 0};
   for (int b = tid; b < B; b += blockDim.x) {
     const uint64_t key = (static_cast<uint64_t>(keys[b]) << 32) | static_cast<uint64_t>(b);
     const int lv = key < thr[0] ? 1 : (key < thr[1] ? 2 : 3);
     levels[b] = static_cast<uint8_t>(lv);
-    const int bw = b % g.nBW, bh = (b / g.nBW) % g.nBH, bf = b / (g.nBW * g.nBH);
-    my[lv - 1] += axis_tokens(bf, tpbF, Ft) * axis_tokens(bh, tpbH, Ht) * axis_tokens(bw, tpbW, Wt);
+    my[lv - 1] += static_cast<uint32_t>(tokcnt[b]);
   }
-  for (int i = 0; i < 3; ++i)
-    if (my[i]) atomicAdd(&tok[i], my[i]);
+  for (int i = 0; i < 3; ++i) {
+    const uint32_t wsum = __shfl(wave_inclusive_scan(my[i]), kWave - 1, kWave);
+    if (tid % kWave == 0 && wsum) atomicAdd(&tok[i], static_cast<int>(wsum));
+  }
   __syncthreads();
   if (tid < 3) counts[tid] = tok[tid];
 }
@@ -374,7 +484,8 @@ bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int
   if (B > kMaxBlocks) return false;
   a.B = static_cast<int>(B);
   a.R = (bH % 8 == 0) ? 8 : (bH % 4 == 0) ? 4 : (bH % 2 == 0) ? 2 : 1;
-  a.fast = K <= 8 && a.R >= 2 && bW <= kWave - 1;
+  const long long lat_bytes = static_cast<long long>(K) * C * F * H * W * 4;
+  a.fast = K <= 8 && a.R >= 2 && bW <= kWave - 1 && lat_bytes < (1LL << 32);
   if (a.fast) {
     a.G = bH / a.R;
     a.CW = ((kWave - 1) / bW) * bW;
@@ -392,7 +503,8 @@ bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int
 }
 
 size_t analyze_ws_bytes(const AnalyzeGeom &g) {
-  return static_cast<size_t>(g.C) * g.G * g.B * sizeof(double);
+  // fp64 partials [C*G][B], then int32 token counts [B]
+  return static_cast<size_t>(g.C) * g.G * g.B * sizeof(double) + static_cast<size_t>(g.B) * 4;
 }
 
 hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nSM, float *scores,
@@ -415,7 +527,12 @@ hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nS
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(levels_kernel, dim3(1), dim3(kLevelsThreads), 0, s, part, g, nS, nSM, scores,
+  int32_t *tokcnt = reinterpret_cast<int32_t *>(part + static_cast<size_t>(g.C) * g.G * g.B);
+  hipLaunchKernelGGL(block_scores_kernel, dim3((g.B + 255) / 256), dim3(256), 0, s, part, g, scores,
+                     tokcnt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(levels_kernel, dim3(1), dim3(kLevelsThreads), 0, s, scores, tokcnt, g.B, nS, nSM,
                      levels, counts);
   return hipGetLastError();
 }

@@ -8,22 +8,21 @@
 //
 //   out[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,h,:] * scale) V[j,h,:]
 //
-// Design:
-//   * grid = (query tiles of BM, heads); x runs fastest, so the workgroups of
-//     one head are dispatched together and share that head's K/V in L2/MALL.
-//   * 4 waves x 32 queries; each wave keeps its queries' Q fragments in
-//     registers for the whole key loop.
-//   * Per key tile of BN = 64: K (row-major, padded rows) and V (transposed to
-//     [dim][key], padded) are staged in LDS, double-buffered: the global loads
-//     of tile j+1 are in flight while tile j is computed.
+// Design (common to both kernels):
+//   * grid = (query tiles, heads); x runs fastest, so the workgroups of one
+//     head are dispatched together and share that head's K/V in L2/MALL.
+//   * each wave owns 32 queries and keeps their Q fragments in registers for
+//     the whole key loop; keys are processed in tiles of 64 staged in LDS.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N).
 //     In the accumulator layout a lane owns one query column, so the online
 //     softmax (running max, rescale, exp2, row sum) is lane-local apart from
 //     one exchange with the lane 32 apart that holds the other key half.
 //   * O^T += V^T P^T: the bf16-converted P accumulators are the B operand
-//     as they stand; the V^T operand is read from the transposed LDS tile in
-//     the same key order, so no data moves through LDS for P.
+//     as they stand; the V^T operand is read from LDS in the same key order,
+//     so no data moves through LDS for P.
 //   * fp32 accumulation, fp32 online softmax in the log2 domain.
+// The d = 64 kernel (attn_fwd_kernel<64>) is the simple form: 4 waves,
+// register-staged double-buffered tiles, V transposed on the LDS write.
 #include <math.h>
 
 #include "common.hpp"
@@ -214,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// d = 128 kernel: 8 waves x 32 queries, K/V tiles of 64 keys brought from
-// global memory straight into LDS (global_load_lds_dwordx4, no registers),
-// three LDS stages so two tiles are in flight while one is computed.
+// d = 128 kernel (attn_fwd_d128_kernel): 8 waves x 32 queries; K/V tiles of
+// 64 keys are brought from global memory straight into LDS
+// (global_load_lds_dwordx4, no registers involved).
 //
 // LDS rows are 256 bytes (128 bf16) split in 16 chunks of 16 bytes; chunk c of
 // row r is stored at slot c ^ swz(r):
@@ -236,7 +235,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t *__re
 // ---------------------------------------------------------------------------
 constexpr int kW2 = 8;                      // waves per workgroup
 constexpr int kBM2 = kW2 * kQW;             // 256 queries per workgroup
-constexpr int kStages = 3;
 constexpr int kRowB = 256;                  // bytes per K/V row (d = 128)
 constexpr int kTileB = kBN * kRowB;         // 16 KB per K or V tile
 constexpr float kRescaleSlack = 8.0f;       // log2 headroom before rescaling
@@ -286,11 +284,27 @@ __device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *V
   }
 }
 
+// ---------------------------------------------------------------------------
+// Schedule of the d = 128 kernel ("ping-pong"): the two waves that share a
+// SIMD run the work of an iteration in opposite order so that one wave's
+// softmax (VALU) executes while the other wave keeps the matrix core busy:
+//   iteration j, MFMA block:  S(j) = K_j Q^T  and  O += V_{j-1} P(j-1)
+//                VALU block:  P = softmax of the newest S (lazy rescale)
+//   first wave of a SIMD: MFMA block, then VALU block (P(j) from S(j));
+//   second wave:          VALU block (P(j-1) from S(j-1)), then MFMA block.
+// Both read K_j and V_{j-1} in iteration j. Four LDS stages: tile t lives in
+// stage t % 4 and is fetched two iterations ahead. The arithmetic of every
+// wave is the same in either order, so the result does not depend on which
+// wave lands on which SIMD.
+// ---------------------------------------------------------------------------
+constexpr int kStagesPP = 4;
+
 __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds[kStagesPP][2][kTileB];
+  __shared__ int simd_slots[4];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -302,9 +316,20 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   const uint16_t *Vh = V + static_cast<size_t>(head) * D;
   const int ntiles = (N + kBN - 1) / kBN;
 
-  // start the first two tiles before anything else
   issue_tile(Kh, Vh, rs, N, 0, lds[0][0], lds[0][1], wave, lane);
   if (ntiles > 1) issue_tile(Kh, Vh, rs, N, kBN, lds[1][0], lds[1][1], wave, lane);
+
+  // which of the (normally two) waves on this SIMD am I?
+  if (tid < 4) simd_slots[tid] = 0;
+  __syncthreads();
+  int slot = 0;
+  {
+    // HW_ID register (id 4), bits [5:4] = SIMD id on gfx9-family parts
+    const int simd = (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;
+    if (lane == 0) slot = atomicAdd(&simd_slots[simd], 1);
+    slot = __shfl(slot, 0, kWave);
+  }
+  const bool second = (slot & 1) != 0;
 
   const int qrow = blockIdx.x * kBM2 + wave * kQW + l32;
   bf16x8 qf[D / 16];
@@ -314,11 +339,23 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
       qf[t] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qp + 16 * t)));
-    // Consume the Q fragments here, so the compiler completes their loads
-    // before the key loop instead of leaving vmcnt waits inside it (where
-    // vmcnt counts the tile copies).
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) asm volatile("" : : "v"(qf[t]));
+  }
+
+  // Tile-invariant per-lane LDS offsets (bytes within a K or V tile).
+  int kl[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) kl[t] = l32 * kRowB + (((2 * t + hf) ^ (l32 & 15)) << 4);
+  // V^T reads: key 16t + 8h2 + 4(grp/2) + gi/4; swz_v(key) does not depend on t.
+  int vl[D / 32][2];
+  const int vchunk = 2 * (grp % 2) + (gi % 4) / 2;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int key0 = 8 * h2 + 4 * (grp / 2) + gi / 4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vl[db][h2] = key0 * kRowB + 8 * (gi % 2) + (((4 * db + vchunk) ^ swz_v(key0)) << 4);
   }
 
   f32x16 o[D / 32];
@@ -327,73 +364,65 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
-
-  // per-lane LDS byte offsets that do not depend on the tile
-  int koff[kBN / 32][D / 16];
+  f32x16 s[kBN / 32];
 #pragma unroll
   for (int mb = 0; mb < kBN / 32; ++mb)
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const int r = mb * 32 + l32;
-      koff[mb][t] = r * kRowB + (((2 * t + hf) ^ swz_k(r)) * 16);
-    }
-  // V^T reads: key k0 + gi/4 with k0 = 16t + 4*(grp/2) (+8 for the second
-  // half), dims 32*db + 16*(grp%2) + 4*(gi%4) .. +3
-  int voff[kBN / 16][2];
-#pragma unroll
-  for (int t = 0; t < kBN / 16; ++t)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int key = 16 * t + 8 * h2 + 4 * (grp / 2) + gi / 4;
-      voff[t][h2] = key * kRowB + 8 * (gi % 2);
-    }
-  const int vchunk = 2 * (grp % 2) + (gi % 4) / 2;   // chunk within a 32-dim block
+    for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+  bf16x8 pb[kBN / 16];
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j % kStages;
-    // This wave's loads of tile j are complete once at most the 4 loads of
-    // tile j+1 are outstanding; the barrier then makes every wave's part of
-    // tile j visible and guarantees stage (j+2)%3 (read in iteration j-1) is
-    // no longer in use.
-    if (j + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __builtin_amdgcn_s_barrier();
-    if (j + 2 < ntiles) {
-      const int s2 = (j + 2) % kStages;
-      issue_tile(Kh, Vh, rs, N, (j + 2) * kBN, lds[s2][0], lds[s2][1], wave, lane);
-    }
-    const char *kb = lds[st][0];
-    const char *vb = lds[st][1];
-
-    f32x16 s[kBN / 32];
+  auto mfma_block = [&](int j) {
+    if (j < ntiles) {
+      const char *kb = lds[j % kStagesPP][0];
 #pragma unroll
-    for (int mb = 0; mb < kBN / 32; ++mb) {
+      for (int mb = 0; mb < kBN / 32; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + koff[mb][t]);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[t], s[mb], 0, 0, 0);
+        for (int t = 0; t < D / 16; ++t) {
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + mb * 32 * kRowB + kl[t]);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[t], s[mb], 0, 0, 0);
+        }
       }
     }
-    if ((j + 1) * kBN > N) {
+    if (j >= 1) {
+      const char *vb = lds[(j - 1) % kStagesPP][1];
+#pragma unroll
+      for (int t = 0; t < kBN / 16; ++t)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4 *)(vb + t * 16 * kRowB + vl[db][0]));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4 *)(vb + t * 16 * kRowB + vl[db][1]));
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
+        }
+    }
+  };
+
+  // softmax of tile jj held in s[] -> pb[] (bf16 B operands of the PV MFMA)
+  auto valu_block = [&](int jj) {
+    if ((jj + 1) * kBN > N) {
 #pragma unroll
       for (int mb = 0; mb < kBN / 32; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * kBN + mb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
+          const int key = jj * kBN + mb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
           if (key >= N) s[mb][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // tree reductions keep the dependency chains short
+    float mx4[4];
 #pragma unroll
-    for (int mb = 0; mb < kBN / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    for (int i = 0; i < 4; ++i) {
+      const f32x16 &sv = s[i / 2];
+      const int b = 8 * (i % 2);
+      mx4[i] = fmaxf(fmaxf(fmaxf(sv[b], sv[b + 1]), fmaxf(sv[b + 2], sv[b + 3])),
+                     fmaxf(fmaxf(sv[b + 4], sv[b + 5]), fmaxf(sv[b + 6], sv[b + 7])));
+    }
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scale_log2;
-    // lazy rescale: keep the running max unless it grew by more than the slack
     const bool grow = mx > m_run + kRescaleSlack;
     if (__ballot(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -405,35 +434,39 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-#pragma unroll
-    for (int mb = 0; mb < kBN / 32; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m_run));
-        s[mb][r] = p;
-        l_run += p;
-      }
-
+    float ls[kBN / 16];
 #pragma unroll
     for (int t = 0; t < kBN / 16; ++t) {
-      const f32x16 &sv = s[t / 2];
-      const int r0 = 8 * (t % 2);
-      const f32x8 pf = {sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3],
-                        sv[r0 + 4], sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]};
-      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+      f32x8 pf;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        bf16x4 part[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int key = 16 * t + 8 * h2 + 4 * (grp / 2) + gi / 4;
-          const int off = voff[t][h2] + (((4 * db + vchunk) ^ swz_v(key)) * 16);
-          part[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vb + off));
-        }
-        const bf16x8 a = {part[0][0], part[0][1], part[0][2], part[0][3],
-                          part[1][0], part[1][1], part[1][2], part[1][3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e)
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(s[t / 2][8 * (t % 2) + e], scale_log2, -m_run));
+      ls[t] = ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+      pb[t] = __builtin_convertvector(pf, bf16x8);
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  for (int j = 0; j <= ntiles; ++j) {
+    if (j < ntiles) {
+      if (j + 1 < ntiles)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    __builtin_amdgcn_s_barrier();
+    if (j + 2 < ntiles) {
+      const int s2 = (j + 2) % kStagesPP;
+      issue_tile(Kh, Vh, rs, N, (j + 2) * kBN, lds[s2][0], lds[s2][1], wave, lane);
+    }
+    if (!second) {
+      mfma_block(j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < ntiles) valu_block(j);
+    } else {
+      if (j >= 1) valu_block(j - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(j);
     }
   }
 
