@@ -249,6 +249,8 @@ def main():
     ap.add_argument("--frac", type=float, default=0.25)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline fraction only")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -263,6 +265,15 @@ def main():
     torch.cuda.set_device(0)
     cfg = configs.V720
     N, H, d = cfg.N, cfg.heads, cfg.d
+    if args.calibrate_copy:
+        # a copy of known size: 1 GiB read + 1 GiB written per dispatch
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: calibration copy of %d bytes done" % (src.numel() * 2), file=sys.stderr, flush=True)
+        del src, dst
     print("bench: generating %s inputs" % cfg.name, file=sys.stderr, flush=True)
     Qb, Kb, Vb = synth.qkv_bits(cfg)
     Q, K, V = (upload_bf16(torch, b) for b in (Qb, Kb, Vb))

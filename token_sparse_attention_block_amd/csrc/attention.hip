@@ -9,8 +9,9 @@
 //   out[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,h,:] * scale) V[j,h,:]
 //
 // Design (common to both kernels):
-//   * grid = (query tiles, heads); x runs fastest, so the workgroups of one
-//     head are dispatched together and share that head's K/V in L2/MALL.
+//   * grid = (query tiles, heads); the d = 128 kernel renumbers workgroups
+//     so that each XCD (one L2 each) works through whole heads, and the
+//     workgroups of a head share its K/V stream in one L2.
 //   * each wave owns 32 queries and keeps their Q fragments in registers for
 //     the whole key loop; keys are processed in tiles of 64 staged in LDS.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N).
@@ -298,6 +299,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *V
 // wave lands on which SIMD.
 // ---------------------------------------------------------------------------
 constexpr int kStagesPP = 4;
+constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
 
 __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
@@ -310,7 +312,15 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   const int wave = tid / kWave, lane = tid % kWave;
   const int l32 = lane & 31, hf = lane >> 5;
   const int grp = lane / 16, gi = lane % 16;
-  const int head = blockIdx.y;
+  // Workgroups are dispatched round-robin over the XCDs (one L2 each).
+  // Renumber them so each XCD works through whole heads: the workgroups of a
+  // head then stream its K/V through a single L2.
+  const int nwg = gridDim.x * gridDim.y;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int xcd = lin % kXcdsAttn, xslot = lin / kXcdsAttn;
+  const int logical = xcd * (nwg / kXcdsAttn) + min(xcd, nwg % kXcdsAttn) + xslot;
+  const int qtile = logical % gridDim.x;
+  const int head = logical / gridDim.x;
   const size_t rs = static_cast<size_t>(H) * D;
   const uint16_t *Kh = K + static_cast<size_t>(head) * D;
   const uint16_t *Vh = V + static_cast<size_t>(head) * D;
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   }
   const bool second = (slot & 1) != 0;
 
-  const int qrow = blockIdx.x * kBM2 + wave * kQW + l32;
+  const int qrow = qtile * kBM2 + wave * kQW + l32;
   bf16x8 qf[D / 16];
   {
     const uint16_t *qp = Q + static_cast<size_t>(min(qrow, nq - 1)) * rs +
