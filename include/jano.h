@@ -144,8 +144,10 @@ int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t 
  * (nl problem statement; fr §1); order of keys/values is irrelevant
  * (nl methodology §2).
  *   Q [n_q][H][d], Kc, Vc [N][H][d], out (out) [n_q][H][d], all bf16;
- *   d in {64, 128}; scale <= 0 selects 1/sqrt(d). bf16 MFMA products, fp32
- *   accumulation and online softmax. n_q == 0 is a no-op; N >= 1.
+ *   d in {64, 128}; scale <= 0 selects 1/sqrt(d); a non-finite scale is
+ *   JANO_E_INVAL. Q, Kc, Vc must hold finite values (NaN/Inf inputs give
+ *   unspecified outputs). bf16 MFMA products, fp32 accumulation and online
+ *   softmax. n_q == 0 is a no-op; N >= 1.
  */
 int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream);

@@ -135,6 +135,7 @@ def test_rows_and_attention_argument_errors():
     assert L.jano_attention(f, 4, f, f, 0, 2, 64, 0.0, f, None) == -1
     assert L.jano_attention(f, 4, f, f, 10, 0, 64, 0.0, f, None) == -1
     assert L.jano_attention(f, 4, f, f, 10, 2, 64, float("nan"), f, None) == -1
+    assert L.jano_attention(f, 4, f, f, 10, 2, 64, float("inf"), f, None) == -1
     assert L.jano_attention(n, 0, f, f, 10, 2, 64, 0.0, n, None) == 0
     assert L.jano_attn_step(f, f, f, f, 11, f, f, 10, 2, 64, 0.0, f, None) == -1
     assert L.jano_attn_step(f, f, f, f, 4, f, f, 10, 2, 80, 0.0, f, None) == -2

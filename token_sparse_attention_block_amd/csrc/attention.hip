@@ -8,22 +8,22 @@
 //
 //   out[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,h,:] * scale) V[j,h,:]
 //
-// Design (common to both kernels):
-//   * grid = (query tiles, heads); the d = 128 kernel renumbers workgroups
-//     so that each XCD (one L2 each) works through whole heads, and the
-//     workgroups of a head share its K/V stream in one L2.
-//   * each wave owns 32 queries and keeps their Q fragments in registers for
-//     the whole key loop; keys are processed in tiles of 64 staged in LDS.
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N).
-//     In the accumulator layout a lane owns one query column, so the online
-//     softmax (running max, rescale, exp2, row sum) is lane-local apart from
-//     one exchange with the lane 32 apart that holds the other key half.
-//   * O^T += V^T P^T: the bf16-converted P accumulators are the B operand
-//     as they stand; the V^T operand is read from LDS in the same key order,
-//     so no data moves through LDS for P.
+// Common design:
+//   * grid = (query tiles, heads); each workgroup streams the whole K/V of one
+//     head through LDS in tiles of 64 keys while its waves keep their Q
+//     fragments in registers for the whole key loop.
+//   * S^T = K Q^T on MFMA with keys on M and queries on N: in the accumulator
+//     layout a lane owns one query column, so the online softmax (running max,
+//     rescale, exp2, row sum) is lane-local apart from a few lane exchanges
+//     between the lanes that hold other keys of the same query.
+//   * O^T += V^T P^T: the bf16-converted P accumulators are the B operand as
+//     they stand and V^T is read from LDS in the same key order, so P never
+//     passes through LDS.
 //   * fp32 accumulation, fp32 online softmax in the log2 domain.
-// The d = 64 kernel (attn_fwd_kernel<64>) is the simple form: 4 waves,
-// register-staged double-buffered tiles, V transposed on the LDS write.
+// attn_fwd_kernel<64> (d = 64) is the simple form: 4 waves x 32 queries,
+// v_mfma_f32_32x32x16_bf16, register-staged double-buffered tiles, V
+// transposed on the LDS write. attn_fwd_d128_kernel (d = 128) is the tuned
+// one, described above its definition.
 #include <math.h>
 
 #include "common.hpp"
@@ -214,19 +214,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// d = 128 kernel (attn_fwd_d128_kernel): 8 waves x 32 queries; K/V tiles of
-// 64 keys are brought from global memory straight into LDS
-// (global_load_lds_dwordx4, no registers involved).
+// Shared pieces of the d = 128 kernel. K/V tiles of 64 keys go from global
+// memory straight into LDS (global_load_lds_dwordx4, no registers involved),
+// four stages deep, two tiles in flight ahead of the one being consumed.
 //
 // LDS rows are 256 bytes (128 bf16) split in 16 chunks of 16 bytes; chunk c of
-// row r is stored at slot c ^ swz(r):
-//   K: swz(r) = r & 15 -- the S MFMA reads one chunk of 16 consecutive rows
-//      per 16 lanes (ds_read_b128), which then hit 16 different bank groups;
-//   V: swz(r) = 4*(r & 3) ^ ((r >> 2) & 3) -- the transposing reads
-//      (ds_read_b64_tr_b16) touch 4 consecutive rows x 4 chunks per half wave,
-//      which this maps onto 16 different bank groups.
-// The swizzle is applied on the global side: the lane that fills LDS slot s
-// fetches the chunk that belongs there.
+// row r is stored at slot c ^ swz(r). The swizzle is applied on the global
+// side: the lane that fills LDS slot s fetches the chunk that belongs there.
 //
 // ds_read_b64_tr_b16 (per 16-lane group): lane j receives element (j % 4) of
 // the 4-element row that source lane 4e + j/4 addressed, for e = 0..3. When
@@ -235,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t *__re
 // the PV MFMA, read from row-major V.
 // ---------------------------------------------------------------------------
 constexpr int kW2 = 8;                      // waves per workgroup
-constexpr int kBM2 = kW2 * kQW;             // 256 queries per workgroup
 constexpr int kRowB = 256;                  // bytes per K/V row (d = 128)
 constexpr int kTileB = kBN * kRowB;         // 16 KB per K or V tile
 constexpr float kRescaleSlack = 8.0f;       // log2 headroom before rescaling
@@ -247,7 +240,6 @@ constexpr int kWaitVmcnt4 = 0x0F74;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
-__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) ^ ((r >> 2) & 3); }
 
 // One global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // lds_base + 16*i. Issued from asm so that the compiler does not treat every
@@ -267,54 +259,64 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane(a);
 }
 
-// Each wave fills 4 KB of a stage: 2 x 1 KB of K rows and 2 x 1 KB of V rows.
-__device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *Vh, size_t rs,
-                                           int N, int key0, char *stage_k, char *stage_v,
-                                           int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * (2 * wave + i) + lane / 16;    // tile row filled by this lane
-    const int slot = lane % 16;
-    const int key = min(key0 + r, N - 1);            // past-the-end rows: finite stand-ins
-    const uint16_t *krow = Kh + static_cast<size_t>(key) * rs;
-    const uint16_t *vrow = Vh + static_cast<size_t>(key) * rs;
-    char *kd = stage_k + (4 * (2 * wave + i)) * kRowB;
-    char *vd = stage_v + (4 * (2 * wave + i)) * kRowB;
-    copy16_to_lds(krow + 8 * (slot ^ swz_k(r)), lds_addr(kd));
-    copy16_to_lds(vrow + 8 * (slot ^ swz_v(r)), lds_addr(vd));
-  }
-}
+
+constexpr int kStages = 4;
+constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
 
 // ---------------------------------------------------------------------------
-// Schedule of the d = 128 kernel ("ping-pong"): the two waves that share a
-// SIMD run the work of an iteration in opposite order so that one wave's
-// softmax (VALU) executes while the other wave keeps the matrix core busy:
-//   iteration j, MFMA block:  S(j) = K_j Q^T  and  O += V_{j-1} P(j-1)
-//                VALU block:  P = softmax of the newest S (lazy rescale)
-//   first wave of a SIMD: MFMA block, then VALU block (P(j) from S(j));
-//   second wave:          VALU block (P(j-1) from S(j-1)), then MFMA block.
-// Both read K_j and V_{j-1} in iteration j. Four LDS stages: tile t lives in
-// stage t % 4 and is fetched two iterations ahead. The arithmetic of every
-// wave is the same in either order, so the result does not depend on which
-// wave lands on which SIMD.
+// attn_fwd_d128_kernel, v_mfma_f32_16x16x32_bf16: 8 waves x 48 queries (three groups of
+// 16 per wave). Every K fragment (16 keys x 32 dims) and V^T fragment (16 dims
+// x 32 keys) read from LDS feeds one MFMA per query group, so a wave reuses
+// each LDS byte for 48 queries instead of 32.
+//   S^T block (16 keys x 16 queries): lane l holds query l%16, keys
+//     4*(l/16) + 0..3 of the block.
+//   PV step of 32 keys: the B operand P^T of lane l takes keys 4h..4h+3 and
+//     16+4h..16+4h+3 (h = l/16) -- registers 0..3 of two consecutive S^T
+//     blocks -- and the V^T operand is read with two transposing reads of
+//     the same keys for dims 16*db + l%16.
+//   K rows use swz(r) = r & 15: the S MFMA reads one chunk of 16 consecutive
+//   rows per 16 lanes (ds_read_b128), which then hit 16 different bank
+//   groups. V rows use swz(r) = 2*(r & 7): the transposing reads of one half
+//   wave cover 8 consecutive rows x 2 chunks, which this spreads over 16 bank
+//   groups.
+//   Workgroups are renumbered so that each XCD (one L2 each) works through
+//   whole heads and the workgroups of a head share its K/V stream in one L2.
+//   The running max is raised only when a tile's max exceeds it by more than
+//   2^8 (kRescaleSlack), so most tiles skip the O rescale; P <= 2^8 stays well
+//   inside bf16 and fp32 range, and the final division by the row sum cancels
+//   whatever reference point the exponents used.
 // ---------------------------------------------------------------------------
-constexpr int kStagesPP = 4;
-constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
+constexpr int kQW2 = 48;                    // queries per wave
+constexpr int kBM2 = kW2 * kQW2;           // 384 queries per workgroup
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz_v2(int r) { return 2 * (r & 7); }
+
+__device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *Vh, size_t rs,
+                                               int N, int key0, char *stage_k, char *stage_v,
+                                               int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + lane / 16;
+    const int slot = lane % 16;
+    const int key = min(key0 + r, N - 1);
+    const uint16_t *krow = Kh + static_cast<size_t>(key) * rs;
+    const uint16_t *vrow = Vh + static_cast<size_t>(key) * rs;
+    copy16_to_lds(krow + 8 * (slot ^ swz_k(r)), lds_addr(stage_k + (4 * (2 * wave + i)) * kRowB));
+    copy16_to_lds(vrow + 8 * (slot ^ swz_v2(r)), lds_addr(stage_v + (4 * (2 * wave + i)) * kRowB));
+  }
+}
 
 __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) char lds[kStagesPP][2][kTileB];
-  __shared__ int simd_slots[4];
+  constexpr int G = 3;                      // query groups of 16
+  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int grp = lane / 16, gi = lane % 16;
-  // Workgroups are dispatched round-robin over the XCDs (one L2 each).
-  // Renumber them so each XCD works through whole heads: the workgroups of a
-  // head then stream its K/V through a single L2.
+  const int l16 = lane & 15, h4 = lane >> 4;
   const int nwg = gridDim.x * gridDim.y;
   const int lin = blockIdx.y * gridDim.x + blockIdx.x;
   const int xcd = lin % kXcdsAttn, xslot = lin / kXcdsAttn;
@@ -329,170 +331,149 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   issue_tile(Kh, Vh, rs, N, 0, lds[0][0], lds[0][1], wave, lane);
   if (ntiles > 1) issue_tile(Kh, Vh, rs, N, kBN, lds[1][0], lds[1][1], wave, lane);
 
-  // which of the (normally two) waves on this SIMD am I?
-  if (tid < 4) simd_slots[tid] = 0;
-  __syncthreads();
-  int slot = 0;
-  {
-    // HW_ID register (id 4), bits [5:4] = SIMD id on gfx9-family parts
-    const int simd = (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;
-    if (lane == 0) slot = atomicAdd(&simd_slots[simd], 1);
-    slot = __shfl(slot, 0, kWave);
+  int qrow[G];
+  bf16x8 qf[G][D / 32];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qrow[g] = qtile * kBM2 + wave * kQW2 + 16 * g + l16;
+    const uint16_t *qp = Q + static_cast<size_t>(min(qrow[g], nq - 1)) * rs +
+                         static_cast<size_t>(head) * D + 8 * h4;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+      qf[g][t] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qp + 32 * t)));
   }
-  const bool second = (slot & 1) != 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) asm volatile("" : : "v"(qf[g][t]));
 
-  const int qrow = qtile * kBM2 + wave * kQW + l32;
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t *qp = Q + static_cast<size_t>(min(qrow, nq - 1)) * rs +
-                         static_cast<size_t>(head) * D + 8 * hf;
+  // tile-invariant LDS byte offsets
+  int kl[D / 32];                            // K: row l16 (+16*kb), chunk 4t + h4
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      qf[t] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qp + 16 * t)));
+  for (int t = 0; t < D / 32; ++t) kl[t] = l16 * kRowB + (((4 * t + h4) ^ swz_k(l16)) << 4);
+  // V^T: key k0 + l16/4 (k0 = 32*ks + 16*half + 4*h4), dims 16*db + 4*(l16%4)
+  const int vkey = 4 * h4 + l16 / 4;         // key within a 16-key half, < 16
+  int vl[D / 16];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) asm volatile("" : : "v"(qf[t]));
+  for (int db = 0; db < D / 16; ++db)
+    vl[db] = vkey * kRowB + 8 * (l16 % 2) + (((2 * db + (l16 % 4) / 2) ^ swz_v2(vkey)) << 4);
+  // rows 16*half + 32*ks + vkey share (r & 7) with vkey, so only the row
+  // offset changes between the four reads of a dim block
+
+  f32x4v o[G][D / 16];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[g][db][r] = 0.0f;
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.0f;
   }
 
-  // Tile-invariant per-lane LDS offsets (bytes within a K or V tile).
-  int kl[D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) kl[t] = l32 * kRowB + (((2 * t + hf) ^ (l32 & 15)) << 4);
-  // V^T reads: key 16t + 8h2 + 4(grp/2) + gi/4; swz_v(key) does not depend on t.
-  int vl[D / 32][2];
-  const int vchunk = 2 * (grp % 2) + (gi % 4) / 2;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const int key0 = 8 * h2 + 4 * (grp / 2) + gi / 4;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      vl[db][h2] = key0 * kRowB + 8 * (gi % 2) + (((4 * db + vchunk) ^ swz_v(key0)) << 4);
-  }
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 s[kBN / 32];
-#pragma unroll
-  for (int mb = 0; mb < kBN / 32; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
-  bf16x8 pb[kBN / 16];
-
-  auto mfma_block = [&](int j) {
-    if (j < ntiles) {
-      const char *kb = lds[j % kStagesPP][0];
-#pragma unroll
-      for (int mb = 0; mb < kBN / 32; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mb][r] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + mb * 32 * kRowB + kl[t]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[t], s[mb], 0, 0, 0);
-        }
-      }
-    }
-    if (j >= 1) {
-      const char *vb = lds[(j - 1) % kStagesPP][1];
-#pragma unroll
-      for (int t = 0; t < kBN / 16; ++t)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4 *)(vb + t * 16 * kRowB + vl[db][0]));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4 *)(vb + t * 16 * kRowB + vl[db][1]));
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], o[db], 0, 0, 0);
-        }
-    }
-  };
-
-  // softmax of tile jj held in s[] -> pb[] (bf16 B operands of the PV MFMA)
-  auto valu_block = [&](int jj) {
-    if ((jj + 1) * kBN > N) {
-#pragma unroll
-      for (int mb = 0; mb < kBN / 32; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = jj * kBN + mb * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-          if (key >= N) s[mb][r] = -INFINITY;
-        }
-    }
-    // tree reductions keep the dependency chains short
-    float mx4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x16 &sv = s[i / 2];
-      const int b = 8 * (i % 2);
-      mx4[i] = fmaxf(fmaxf(fmaxf(sv[b], sv[b + 1]), fmaxf(sv[b + 2], sv[b + 3])),
-                     fmaxf(fmaxf(sv[b + 4], sv[b + 5]), fmaxf(sv[b + 6], sv[b + 7])));
-    }
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scale_log2;
-    const bool grow = mx > m_run + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    float ls[kBN / 16];
-#pragma unroll
-    for (int t = 0; t < kBN / 16; ++t) {
-      f32x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[e] = __builtin_amdgcn_exp2f(fmaf(s[t / 2][8 * (t % 2) + e], scale_log2, -m_run));
-      ls[t] = ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
-      pb[t] = __builtin_convertvector(pf, bf16x8);
-    }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  };
-
-  for (int j = 0; j <= ntiles; ++j) {
-    if (j < ntiles) {
-      if (j + 1 < ntiles)
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
-      else
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j % kStages;
+    if (j + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
     if (j + 2 < ntiles) {
-      const int s2 = (j + 2) % kStagesPP;
+      const int s2 = (j + 2) % kStages;
       issue_tile(Kh, Vh, rs, N, (j + 2) * kBN, lds[s2][0], lds[s2][1], wave, lane);
     }
-    if (!second) {
-      mfma_block(j);
-      __builtin_amdgcn_sched_barrier(0);
-      if (j < ntiles) valu_block(j);
-    } else {
-      if (j >= 1) valu_block(j - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_block(j);
+    const char *kb = lds[st][0];
+    const char *vb = lds[st][1];
+
+    f32x4v s[G][kBN / 16];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int b = 0; b < kBN / 16; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[g][b][r] = 0.0f;
+#pragma unroll
+    for (int b = 0; b < kBN / 16; ++b)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + b * 16 * kRowB + kl[t]);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          s[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[g][t], s[g][b], 0, 0, 0);
+      }
+
+    bf16x8 pb[G][kBN / 32];
+    const bool ragged = (j + 1) * kBN > N;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (ragged) {
+#pragma unroll
+        for (int b = 0; b < kBN / 16; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j * kBN + 16 * b + 4 * h4 + r >= N) s[g][b][r] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[g][0][0], s[g][0][1]), fmaxf(s[g][0][2], s[g][0][3])),
+                       fmaxf(fmaxf(s[g][1][0], s[g][1][1]), fmaxf(s[g][1][2], s[g][1][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[g][2][0], s[g][2][1]), fmaxf(s[g][2][2], s[g][2][3])),
+                           fmaxf(fmaxf(s[g][3][0], s[g][3][1]), fmaxf(s[g][3][2], s[g][3][3]))));
+      mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scale_log2;
+      const bool grow = mx > m_run[g] + kRescaleSlack;
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_run[g];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[g][db][r] *= alpha;
+      }
+      float ls[kBN / 32];
+#pragma unroll
+      for (int ks = 0; ks < kBN / 32; ++ks) {
+        f32x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[e] = __builtin_amdgcn_exp2f(fmaf(s[g][2 * ks + e / 4][e % 4], scale_log2, -m_run[g]));
+        ls[ks] = ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
+        pb[g][ks] = __builtin_convertvector(pf, bf16x8);
+      }
+      l_run[g] += ls[0] + ls[1];
     }
+
+#pragma unroll
+    for (int ks = 0; ks < kBN / 32; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(vb + (32 * ks) * kRowB + vl[db]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(vb + (32 * ks + 16) * kRowB + vl[db]));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[g][ks], o[g][db], 0, 0, 0);
+      }
   }
 
-  const float l_tot = l_run + shfl_xor_f32(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (qrow < nq) {
-    uint16_t *op = out + static_cast<size_t>(qrow) * rs + static_cast<size_t>(head) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int g = 0; g < G; ++g) {
+    float l_tot = l_run[g] + shfl_xor_f32(l_run[g], 16);
+    l_tot += shfl_xor_f32(l_tot, 32);
+    const float inv = 1.0f / l_tot;
+    if (qrow[g] < nq) {
+      uint16_t *op = out + static_cast<size_t>(qrow[g]) * rs + static_cast<size_t>(head) * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 v = {o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv, o[db][4 * g4 + 2] * inv,
-                         o[db][4 * g4 + 3] * inv};
-        const bf16x4 b = __builtin_convertvector(v, bf16x4);
-        *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * g4 + 4 * hf) = b;
+      for (int db = 0; db < D / 16; ++db) {
+        const f32x4 v = {o[g][db][0] * inv, o[g][db][1] * inv, o[g][db][2] * inv, o[g][db][3] * inv};
+        *reinterpret_cast<bf16x4 *>(op + 16 * db + 4 * h4) = __builtin_convertvector(v, bf16x4);
       }
+    }
   }
 }
 
@@ -504,8 +485,8 @@ hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, co
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(static_cast<unsigned>((nq + kBM - 1) / kBM), static_cast<unsigned>(H));
   if (d == 128) {
-    const dim3 grid2(static_cast<unsigned>((nq + kBM2 - 1) / kBM2), static_cast<unsigned>(H));
-    hipLaunchKernelGGL(attn_fwd_d128_kernel, grid2, dim3(kW2 * kWave), 0, s, Q, K, V, out,
+    const dim3 grid3(static_cast<unsigned>((nq + kBM2 - 1) / kBM2), static_cast<unsigned>(H));
+    hipLaunchKernelGGL(attn_fwd_d128_kernel, grid3, dim3(kW2 * kWave), 0, s, Q, K, V, out,
                        static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
   } else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, Q, K, V, out,

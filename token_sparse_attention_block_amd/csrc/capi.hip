@@ -138,7 +138,7 @@ int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t 
 
 int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream) {
-  if (N < 1 || H < 1 || n_q < 0 || N > kMaxRows || n_q > kMaxRows || !(scale == scale))
+  if (N < 1 || H < 1 || n_q < 0 || N > kMaxRows || n_q > kMaxRows || !isfinite(scale))
     return JANO_E_INVAL;
   if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
   if (n_q > 0 && (!Q || !out)) return JANO_E_INVAL;
@@ -154,7 +154,7 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
 int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
                    const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
                    int d, float scale, uint16_t *out, void *stream) {
-  if (N < 1 || H < 1 || n_act < 0 || n_act > N || N > kMaxRows || !(scale == scale))
+  if (N < 1 || H < 1 || n_act < 0 || n_act > N || N > kMaxRows || !isfinite(scale))
     return JANO_E_INVAL;
   if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
   if (H > 65535) return JANO_E_UNSUPPORTED;
