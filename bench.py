@@ -15,6 +15,12 @@ queries), the 10/25/50% step speedups and the 50-step interleaved run on the
 the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--frac 0.25] [--no-cpu]
+
+HBM traffic (`roofline.traffic`) comes from profiles/traffic.json, written by
+    python bench.py --ingest-counters FETCH.csv WRITE.csv
+from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
+`bench.py --steps 2 --warmup 0 --no-cpu --no-extra --calibrate-copy`; it is
+used only while the kernel sources still hash to what was profiled.
 """
 import argparse
 import hashlib
@@ -44,7 +50,80 @@ def kernel_source_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_file, workload):
+TRAFFIC_KERNELS = {            # kernel name prefix -> (source file, key)
+    "attn_fwd_d128_kernel": ("attention.hip", "attention"),
+    "gather_rows_v16": ("rows.hip", "gather"),
+    "scatter_kv_v16": ("rows.hip", "scatter"),
+    "analyze_stream_kernel": ("analyze.hip", "analyze_stream"),
+}
+
+
+def _short_kernel_name(name):
+    name = name.replace("void ", "").replace("jano::(anonymous namespace)::", "")
+    return name.split("(")[0].split("<")[0]
+
+
+def ingest_counters(fetch_csv, write_csv, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) -> HBM bytes per launch.
+
+    Each counter is scaled by what it reads for the 1 GiB device copy that
+    --calibrate-copy issues first (the largest __amd_rocclr_copyBuffer
+    dispatch: 1 GiB read, 1 GiB written). In a --no-extra run the attention
+    kernel appears with two grids: the active-query step (smaller) and the
+    dense reference (larger); they are stored as `attention` and
+    `attention_dense`."""
+    import csv
+    import statistics
+
+    def per_group(path, counter):
+        groups = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+                groups.setdefault(k, {}).setdefault(r["Dispatch_Id"], 0.0)
+                groups[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return groups
+
+    fg, wg = per_group(fetch_csv, "FETCH_SIZE"), per_group(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    # the calibration copy is the largest copy dispatch (the cache clones are smaller)
+    copy_f = max(max(v.values()) for (n, _), v in fg.items() if n == "__amd_rocclr_copyBuffer")
+    copy_w = max(max(v.values()) for (n, _), v in wg.items() if n == "__amd_rocclr_copyBuffer")
+    fetch = {k: statistics.median(v.values()) for k, v in fg.items()}
+    write = {k: statistics.median(v.values()) for k, v in wg.items()}
+    f_fac, w_fac = gib_kib / copy_f, gib_kib / copy_w
+    out = {"calibration": {"copy_bytes": 1 << 30, "fetch_kib": copy_f, "write_kib": copy_w,
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)}}
+    for prefix, (src, key) in TRAFFIC_KERNELS.items():
+        grids = sorted(g for (n, g) in fetch if n == prefix)
+        if not grids:
+            continue
+        if key == "attention":
+            if len(grids) != 2:
+                raise SystemExit("expected the active and the dense attention grid, got %s" % grids)
+            named = [("attention", grids[0]), ("attention_dense", grids[1])]
+        else:
+            named = [(key, grids[0])]
+        for name, g in named:
+            fb, wb = fetch[(prefix, g)] * 1024 * f_fac, write[(prefix, g)] * 1024 * w_fac
+            out[name] = {"source": src, "source_sha256_16": kernel_source_hash(src),
+                         "grid_threads": g, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                         "hbm_bytes_per_launch": round(fb + wb)}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    allw = {}
+    if os.path.exists(p):
+        with open(p) as f:
+            allw = json.load(f)
+    allw[workload] = out
+    with open(p, "w") as f:
+        json.dump(allw, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic(key, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, only
     if it was taken on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -52,8 +131,8 @@ def load_traffic(kernel_file, workload):
         return None
     with open(p) as f:
         t = json.load(f)
-    e = t.get(workload, {}).get(kernel_file)
-    if not e or e.get("source_sha256_16") != kernel_source_hash(kernel_file):
+    e = t.get(workload, {}).get(key)
+    if not e or e.get("source_sha256_16") != kernel_source_hash(e["source"]):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -251,7 +330,12 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline fraction only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, "720p-active%d" % round(100 * args.frac))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(heads would shard across GPUs with no exchange inside the path)", file=sys.stderr)
@@ -299,8 +383,10 @@ def main():
                     "GB/s": 4 * n_act * row_bytes / (per["scatter"] * 1e-3) / 1e9},
         "attention": {"ms": per["attention"], "flops": attn_flops, "TFLOP/s": achieved},
     }
+    wl = "720p-active%d" % round(100 * args.frac)
     for k in ("analyze", "gather", "scatter"):
         kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
+        kernels[k]["traffic"] = load_traffic("analyze_stream" if k == "analyze" else k, wl)
     kernels["attention"]["frac_mfma"] = achieved / PEAK_BF16_TFLOPS
     for v in kernels.values():
         for kk in list(v):
@@ -356,7 +442,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
-                     "traffic": load_traffic("attention.hip", "720p-active%d" % round(100 * args.frac)),
+                     "traffic": load_traffic("attention", wl),
                      "kernel": "attn_fwd_d128_kernel"},
         "cpu_baseline": cpu,
         "step_speedup_vs_dense": speedups,
