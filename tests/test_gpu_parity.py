@@ -293,8 +293,12 @@ def test_cached_equals_recompute(torch):
     np.testing.assert_array_equal(host_bits(step), dense[idx])
 
 
+# d = 128 cases cover a cache shorter than one 64-key tile (1, 63), whole
+# tiles only (64, 128), one extra key (65, 129, 4097) and a mid-tile tail
+# (1000); query counts straddle the 384-query workgroup tile.
 @pytest.mark.parametrize("n,N,d", [(1, 1, 64), (31, 100, 64), (129, 65, 128), (200, 1000, 128),
-                                   (64, 129, 64), (257, 4097, 128)])
+                                   (64, 129, 64), (257, 4097, 128), (5, 1, 128), (48, 63, 128),
+                                   (100, 64, 128), (384, 128, 128), (385, 129, 128)])
 def test_attention_ragged(torch, n, N, d):
     print("attention ragged", n, N, d, flush=True)
     rng = np.random.default_rng(n * 7 + N)

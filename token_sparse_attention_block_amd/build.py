@@ -28,8 +28,10 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 # Per-source extras. attention.hip: its inputs are finite by contract (the
 # scores are finite products of finite bf16 values), so the max reductions of
-# the online softmax need no NaN canonicalisation.
-EXTRA = {"attention.hip": ["-fno-honor-nans"]}
+# the online softmax need no NaN canonicalisation; the ILP-first machine
+# scheduler interleaves its MFMA, exp and LDS streams better than the default
+# occupancy-first one (the kernel's occupancy is fixed by its LDS use anyway).
+EXTRA = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:

@@ -26,6 +26,8 @@
 // one, described above its definition.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -253,6 +255,15 @@ __device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_bas
                : "memory", "m0");
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (saddr form): advancing the base costs no vector instructions.
+__device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   const uint32_t a = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
@@ -284,7 +295,15 @@ constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
 //   The running max is raised only when a tile's max exceeds it by more than
 //   2^8 (kRescaleSlack), so most tiles skip the O rescale; P <= 2^8 stays well
 //   inside bf16 and fp32 range, and the final division by the row sum cancels
-//   whatever reference point the exponents used.
+//   whatever reference point the exponents used. Each lane first compares the
+//   max of its own 16 keys; the four lanes of a query exchange maxima (and the
+//   wave rescales) only when some lane's keys would raise the running max.
+//   Row sums are taken over the bf16 P values the PV product uses, two at a
+//   time (v_dot2_f32_bf16 against (1, 1)).
+//   K/V copies of full tiles use a wave-uniform base address and per-lane
+//   32-bit offsets that do not change from tile to tile; only the last tile,
+//   when it extends past N, goes through the clamped per-row path. That tile
+//   is also the only one whose scores are masked (keys >= N get -inf).
 // ---------------------------------------------------------------------------
 constexpr int kQW2 = 48;                    // queries per wave
 constexpr int kBM2 = kW2 * kQW2;           // 384 queries per workgroup
@@ -304,6 +323,18 @@ __device__ __forceinline__ void issue_tile(const uint16_t *Kh, const uint16_t *V
     const uint16_t *vrow = Vh + static_cast<size_t>(key) * rs;
     copy16_to_lds(krow + 8 * (slot ^ swz_k(r)), lds_addr(stage_k + (4 * (2 * wave + i)) * kRowB));
     copy16_to_lds(vrow + 8 * (slot ^ swz_v2(r)), lds_addr(stage_v + (4 * (2 * wave + i)) * kRowB));
+  }
+}
+
+// Full tile (all 64 keys < N): per-lane offsets are tile-invariant.
+// lds_k / lds_v: LDS byte addresses (wave-uniform) of this wave's first row in the stage
+__device__ __forceinline__ void issue_tile_full(const char *kbase, const char *vbase,
+                                                const uint32_t (&koff)[2], const uint32_t (&voff)[2],
+                                                uint32_t lds_k, uint32_t lds_v) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    copy16_to_lds_s(kbase, koff[i], lds_k + 4 * i * kRowB);
+    copy16_to_lds_s(vbase, voff[i], lds_v + 4 * i * kRowB);
   }
 }
 
@@ -327,9 +358,29 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   const uint16_t *Kh = K + static_cast<size_t>(head) * D;
   const uint16_t *Vh = V + static_cast<size_t>(head) * D;
   const int ntiles = (N + kBN - 1) / kBN;
+  const int nfull = N / kBN;
+  // byte offsets of this lane's two copies within a tile (row r, swizzled chunk)
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + lane / 16;
+    const int slot = lane % 16;
+    koff[i] = static_cast<uint32_t>(r * rs * 2 + 16 * (slot ^ swz_k(r)));
+    voff[i] = static_cast<uint32_t>(r * rs * 2 + 16 * (slot ^ swz_v2(r)));
+  }
+  const size_t tile_bytes = static_cast<size_t>(kBN) * rs * 2;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds[0][0]) + 8 * wave * kRowB);
+  auto issue = [&](const int t, const int stg) {
+    if (t < nfull)
+      issue_tile_full(reinterpret_cast<const char *>(Kh) + t * tile_bytes,
+                      reinterpret_cast<const char *>(Vh) + t * tile_bytes, koff, voff,
+                      lds0 + stg * 2 * kTileB, lds0 + stg * 2 * kTileB + kTileB);
+    else
+      issue_tile(Kh, Vh, rs, N, t * kBN, lds[stg][0], lds[stg][1], wave, lane);
+  };
 
-  issue_tile(Kh, Vh, rs, N, 0, lds[0][0], lds[0][1], wave, lane);
-  if (ntiles > 1) issue_tile(Kh, Vh, rs, N, kBN, lds[1][0], lds[1][1], wave, lane);
+  issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
 
   int qrow[G];
   bf16x8 qf[G][D / 32];
@@ -367,6 +418,8 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[g][db][r] = 0.0f;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   float m_run[G], l_run[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -374,17 +427,16 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     l_run[g] = 0.0f;
   }
 
-  for (int j = 0; j < ntiles; ++j) {
+  // one 64-key tile; RAGGED only for a last tile that extends past N
+  auto tile = [&](const int j, auto ragged_tag) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
     const int st = j % kStages;
     if (j + 1 < ntiles)
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
-    if (j + 2 < ntiles) {
-      const int s2 = (j + 2) % kStages;
-      issue_tile(Kh, Vh, rs, N, (j + 2) * kBN, lds[s2][0], lds[s2][1], wave, lane);
-    }
+    if (j + 2 < ntiles) issue(j + 2, (j + 2) % kStages);
     const char *kb = lds[st][0];
     const char *vb = lds[st][1];
 
@@ -406,24 +458,26 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
       }
 
     bf16x8 pb[G][kBN / 32];
-    const bool ragged = (j + 1) * kBN > N;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if (ragged) {
+      if constexpr (RAGGED) {
 #pragma unroll
         for (int b = 0; b < kBN / 16; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (j * kBN + 16 * b + 4 * h4 + r >= N) s[g][b][r] = -INFINITY;
       }
+      // this lane's 16 keys of the query; the 4 lanes that share a query
+      // exchange maxima only when one of them would raise the running max
       float mx = fmaxf(fmaxf(fmaxf(s[g][0][0], s[g][0][1]), fmaxf(s[g][0][2], s[g][0][3])),
                        fmaxf(fmaxf(s[g][1][0], s[g][1][1]), fmaxf(s[g][1][2], s[g][1][3])));
       mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[g][2][0], s[g][2][1]), fmaxf(s[g][2][2], s[g][2][3])),
                            fmaxf(fmaxf(s[g][3][0], s[g][3][1]), fmaxf(s[g][3][2], s[g][3][3]))));
-      mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scale_log2;
-      const bool grow = mx > m_run[g] + kRescaleSlack;
-      if (__ballot(grow)) {
+      mx *= scale_log2;
+      if (__ballot(mx > m_run[g] + kRescaleSlack)) {
+        mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+        const bool grow = mx > m_run[g] + kRescaleSlack;
         const float m_new = grow ? mx : m_run[g];
         const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
         m_run[g] = m_new;
@@ -433,15 +487,20 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[g][db][r] *= alpha;
       }
-      float ls[kBN / 32];
+      float ls[kBN / 32] = {0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < kBN / 32; ++ks) {
         f32x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           pf[e] = __builtin_amdgcn_exp2f(fmaf(s[g][2 * ks + e / 4][e % 4], scale_log2, -m_run[g]));
-        ls[ks] = ((pf[0] + pf[1]) + (pf[2] + pf[3])) + ((pf[4] + pf[5]) + (pf[6] + pf[7]));
         pb[g][ks] = __builtin_convertvector(pf, bf16x8);
+        // row sum of the bf16 P the PV product uses: pairs dotted with (1, 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pp = {pb[g][ks][2 * e], pb[g][ks][2 * e + 1]};
+          ls[ks] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, ls[ks], false);
+        }
       }
       l_run[g] += ls[0] + ls[1];
     }
@@ -459,7 +518,9 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
         for (int g = 0; g < G; ++g)
           o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[g][ks], o[g][db], 0, 0, 0);
       }
-  }
+  };
+  for (int j = 0; j < nfull; ++j) tile(j, std::false_type{});
+  if (nfull < ntiles) tile(nfull, std::true_type{});
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
