@@ -3,8 +3,8 @@
 Workload (default): the 720p video-shaped grid, 21x45x80 = 75600 tokens,
 40 heads, d = 128, bf16; warm-up latents 5 x [16, 21, 90, 160] fp32.
 One step = one pass of the whole path on resident inputs:
-    jano_analyze (block scores + levels, 40/30/30 mix shifted so that the
-    Active level holds the configured share) -> jano_schedule at an
+    jano_analyze_scores (block scores) -> jano_levels (40/30/30 mix shifted
+    so that the Active level holds the configured share) -> jano_schedule at an
     Active-only interleaved step -> jano_gather_rows (active rows of Q) ->
     jano_scatter_kv (fresh K/V rows into the full-sequence cache) ->
     jano_attention (active queries against the whole cache).
@@ -167,8 +167,14 @@ class Path:
                                          sc.periods, self.step_id)
 
     def analyze(self, i):
-        self.jano.analyze(self.lats[i % len(self.lats)], self.spec, self.spm, self.mpm,
-                          self.scores, self.levels, self.counts, self.ws)
+        self.analyze_scores(i)
+        self.levels_()
+
+    def analyze_scores(self, i):
+        self.jano.analyze_scores(self.lats[i % len(self.lats)], self.spec, self.scores, self.ws)
+
+    def levels_(self):
+        self.jano.levels(self.scores, self.spec, self.spm, self.mpm, self.levels, self.counts)
 
     def schedule(self):
         T, W, Cd, per = self.sched
@@ -183,27 +189,23 @@ def make_qkv(torch, synth, cfg):
     return [upload_bf16(torch, b) for b in synth.qkv_bits(cfg)]
 
 
+STEP_CALLS = ("analyze_scores", "levels", "schedule", "gather", "scatter", "attention")
+
+
 def run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, ev=None):
-    """One whole pass; `ev` (list of 6 events) brackets each kernel."""
+    """One whole pass; `ev` (len(STEP_CALLS) + 1 events) brackets each call."""
     jano = p.jano
+    idx = p.idx[:p.n_act]
+    calls = (lambda: p.analyze_scores(i), p.levels_, p.schedule,
+             lambda: jano.gather_rows(Q, idx, p.n_act, out=q_act),
+             lambda: jano.scatter_kv(Kn, Vn, idx, Kc, Vc, n_act=p.n_act),
+             lambda: jano.attention(q_act, Kc, Vc, out=out, n_q=p.n_act))
     if ev:
         ev[0].record()
-    p.analyze(i)
-    if ev:
-        ev[1].record()
-    p.schedule()
-    if ev:
-        ev[2].record()
-    idx = p.idx[:p.n_act]
-    jano.gather_rows(Q, idx, p.n_act, out=q_act)
-    if ev:
-        ev[3].record()
-    jano.scatter_kv(Kn, Vn, idx, Kc, Vc, n_act=p.n_act)
-    if ev:
-        ev[4].record()
-    jano.attention(q_act, Kc, Vc, out=out, n_q=p.n_act)
-    if ev:
-        ev[5].record()
+    for j, call in enumerate(calls):
+        call()
+        if ev:
+            ev[j + 1].record()
 
 
 def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup):
@@ -219,14 +221,14 @@ def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup)
     for i in range(warmup):
         run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out)
     torch.cuda.synchronize()
-    evs = [[_ev(torch) for _ in range(6)] for _ in range(steps)]
+    evs = [[_ev(torch) for _ in range(len(STEP_CALLS) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    names = ("analyze", "schedule", "gather", "scatter", "attention")
-    per = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(names)}
+    per = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(STEP_CALLS)}
+    per["analyze"] = per["analyze_scores"] + per["levels"]
     return p, n, wall * 1e3, per
 
 
@@ -371,11 +373,13 @@ def main():
     attn_flops = 4.0 * n_act * N * H * d
     value = attn_flops / (ms_step * 1e-3) / 1e12
     achieved = attn_flops / (per["attention"] * 1e-3) / 1e12
-    lat_bytes = cfg.latent_bytes + p.B * 5 + 12
+    lat_bytes = cfg.latent_bytes + p.B * 4      # latents read, scores written
     row_bytes = H * d * 2
     kernels = {
-        "analyze": {"ms": per["analyze"], "bytes": lat_bytes,
-                    "GB/s": lat_bytes / (per["analyze"] * 1e-3) / 1e9},
+        "analyze_scores": {"ms": per["analyze_scores"], "bytes": lat_bytes,
+                           "GB/s": lat_bytes / (per["analyze_scores"] * 1e-3) / 1e9},
+        "levels": {"ms": per["levels"]},
+        "analyze": {"ms": per["analyze"]},
         "schedule": {"ms": per["schedule"]},
         "gather": {"ms": per["gather"], "bytes": 2 * n_act * row_bytes,
                    "GB/s": 2 * n_act * row_bytes / (per["gather"] * 1e-3) / 1e9},
@@ -384,9 +388,9 @@ def main():
         "attention": {"ms": per["attention"], "flops": attn_flops, "TFLOP/s": achieved},
     }
     wl = "720p-active%d" % round(100 * args.frac)
-    for k in ("analyze", "gather", "scatter"):
+    for k in ("analyze_scores", "gather", "scatter"):
         kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
-        kernels[k]["traffic"] = load_traffic("analyze_stream" if k == "analyze" else k, wl)
+        kernels[k]["traffic"] = load_traffic("analyze_stream" if k == "analyze_scores" else k, wl)
     kernels["attention"]["frac_mfma"] = achieved / PEAK_BF16_TFLOPS
     for v in kernels.values():
         for kk in list(v):

@@ -81,23 +81,48 @@ int jano_schedule_count(const int32_t *level_tok_counts_host, const jano_sched *
 size_t jano_analyze_workspace_bytes(const jano_grid *g);
 
 /*
- * jano_analyze -- block-wise complexity analyzer plus level bucketing.
+ * jano_analyze_scores -- block-wise complexity analyzer (scores only).
  * Pages: zh technical summary §2.1 (3D blocks, temporal and spatial gradients,
  * second-order difference over the first K steps, one score per block);
- * nl methodology §1 (three convergence levels); fr/pt/ko §2.A.
+ * fr/pt/ko §2.A.
  *
  *   lat               [K][C][F][H][W] fp32, the latents entering steps 0..K-1
- *   static_permille,  share of blocks (per mille, rounded half up) assigned
- *   moderate_permille Static (lowest scores) and Moderate (next); the rest are
- *                     Active. Each in [0, 1000], sum <= 1000.
+ *                     (finite values)
  *   scores   (out)    [B] fp32: mean |D_k(p+e_a) - D_k(p)| over the axes a
  *                     with extent >= 2, k = 1..K-2, all channels and every p
  *                     in the block with p+e_a inside the latent, where
  *                     D_k = L_{k+1} - 2 L_k + L_{k-1} (formed in fp64)
- *   levels   (out)    [B] uint8 in {1,2,3}: blocks ranked by (score, id)
- *   level_tok_counts (out) [3] int32: tokens at level 1, 2, 3
  *   ws, ws_bytes      device workspace of >= jano_analyze_workspace_bytes
  *                     (contents need no initialisation)
+ * Deterministic: the same input gives bit-identical scores.
+ */
+int jano_analyze_scores(const float *lat, const jano_grid *g, float *scores, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * jano_levels -- level bucketing of block scores.
+ * Pages: nl methodology §1 (three convergence levels: static, moderate,
+ * active); zh §2.1.
+ *
+ *   scores            [B] fp32 block scores, finite and >= 0 (as written by
+ *                     jano_analyze_scores)
+ *   static_permille,  share of blocks (per mille, rounded half up) assigned
+ *   moderate_permille Static (lowest scores) and Moderate (next); the rest are
+ *                     Active. Each >= 0, sum <= 1000.
+ *   levels   (out)    [B] uint8 in {1,2,3}: blocks ranked by (score, block id);
+ *                     rank < nS -> 1, rank < nSM -> 2, else 3, with
+ *                     nS = (static_permille*B + 500) / 1000 and
+ *                     nSM = ((static_permille+moderate_permille)*B + 500) / 1000
+ *   level_tok_counts (out) [3] int32: tokens at level 1, 2, 3
+ * Needs no workspace.
+ */
+int jano_levels(const float *scores, const jano_grid *g, int static_permille,
+                int moderate_permille, uint8_t *levels, int32_t *level_tok_counts,
+                void *stream);
+
+/*
+ * jano_analyze -- jano_analyze_scores followed by jano_levels on one stream;
+ * arguments as there.
  */
 int jano_analyze(const float *lat, const jano_grid *g, int static_permille,
                  int moderate_permille, float *scores, uint8_t *levels,

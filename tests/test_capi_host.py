@@ -101,6 +101,18 @@ def test_analyze_argument_errors():
     assert L.jano_analyze(fake, ctypes.byref(g), -1, 300, fake, fake, fake, fake, ws, None) == -1
     assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, fake, ws - 1, None) == -4
     assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, null, ws, None) == -4
+    # the two halves reject the same things
+    assert L.jano_analyze_scores(null, ctypes.byref(g), fake, fake, ws, None) == -1
+    assert L.jano_analyze_scores(fake, ctypes.byref(g), null, fake, ws, None) == -1
+    assert L.jano_analyze_scores(fake, ctypes.byref(g), fake, fake, ws - 1, None) == -4
+    assert L.jano_analyze_scores(fake, ctypes.byref(g), fake, null, ws, None) == -4
+    assert L.jano_levels(null, ctypes.byref(g), 400, 300, fake, fake, None) == -1
+    assert L.jano_levels(fake, ctypes.byref(g), 400, 300, null, fake, None) == -1
+    assert L.jano_levels(fake, ctypes.byref(g), 400, 300, fake, null, None) == -1
+    assert L.jano_levels(fake, ctypes.byref(g), 700, 400, fake, fake, None) == -1
+    assert L.jano_levels(fake, ctypes.byref(g), 400, -1, fake, fake, None) == -1
+    bad = _grid(K=2)
+    assert L.jano_levels(fake, ctypes.byref(bad), 400, 300, fake, fake, None) == -1
 
 
 def test_schedule_argument_errors():

@@ -178,6 +178,53 @@ def test_analyzer_level_mixes(torch, spm, mpm):
     _check_analyzer(lat, spec, s, l, c, spm, mpm)
 
 
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V480, configs.V720],
+                         ids=lambda c: c.name)
+def test_levels_from_oracle_scores(torch, cfg):
+    # jano_levels on the oracle's own fp32 scores: levels and counts bit-exact
+    print("levels", cfg.name, flush=True)
+    spec = jano.GridSpec.of(cfg)
+    lat = synth.latents(cfg, signal=True)
+    ref32 = O.analyze_scores(lat, spec.block)
+    lv, cnt = jano.levels(dev(ref32), spec, cfg.static_permille, cfg.moderate_permille)
+    torch.cuda.synchronize()
+    lv_ref = O.assign_levels(ref32, cfg.static_permille, cfg.moderate_permille)
+    np.testing.assert_array_equal(lv.cpu().numpy(), lv_ref)
+    np.testing.assert_array_equal(
+        cnt.cpu().numpy(), O.level_token_counts(lv_ref, (spec.F, spec.H, spec.W), spec.patch, spec.block))
+
+
+@pytest.mark.parametrize("B_side,nvals", [(4, 3), (37, 5), (128, 1), (128, 1000), (128, 1 << 20)])
+def test_levels_ties_and_max_size(torch, B_side, nvals):
+    # scores with many ties (ordered by block id), one value only, and the
+    # largest block count (128 x 128 = 16384 blocks)
+    print("levels ties", B_side, nvals, flush=True)
+    spec = jano.GridSpec(3, 1, 1, 4 * B_side, 4 * B_side, (1, 4, 4), (1, 1, 1))
+    B = B_side * B_side
+    rng = np.random.default_rng(B_side + nvals)
+    sc = (rng.integers(0, nvals, B) * np.float32(0.125)).astype(np.float32)
+    for spm, mpm in [(400, 300), (0, 1000), (1000, 0), (333, 333)]:
+        lv, cnt = jano.levels(dev(sc), spec, spm, mpm)
+        torch.cuda.synchronize()
+        lv_ref = O.assign_levels(sc, spm, mpm)
+        np.testing.assert_array_equal(lv.cpu().numpy(), lv_ref)
+        np.testing.assert_array_equal(
+            cnt.cpu().numpy(), O.level_token_counts(lv_ref, (spec.F, spec.H, spec.W), spec.patch, spec.block))
+
+
+def test_analyze_scores_entry_point(torch):
+    # the scores-only call equals jano_analyze's scores, bit for bit, every call
+    cfg = configs.V480
+    spec = jano.GridSpec.of(cfg)
+    lat = dev(synth.latents(cfg, signal=True))
+    s_all, _, _ = jano.analyze(lat, spec)
+    s1 = jano.analyze_scores(lat, spec)
+    s2 = jano.analyze_scores(lat, spec)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s1.cpu().numpy(), s_all.cpu().numpy())
+    np.testing.assert_array_equal(s2.cpu().numpy(), s1.cpu().numpy())
+
+
 # ------------------------------------------------------------------ schedule
 
 def test_schedule_all_steps_480p(torch):

@@ -27,9 +27,12 @@
 //
 // Kernel 2 (block_scores_kernel, one thread per block) sums the partials in a
 // fixed order, divides by the closed-form term count and rounds the score to
-// fp32; it also writes the block's token count. Kernel 3 (levels_kernel, one
-// workgroup) finds the two level thresholds of the (score, block id) order by
-// radix select, writes the levels and counts tokens per level.
+// fp32. Kernels 1 and 2 are jano_analyze_scores.
+//
+// Levels (jano_levels): kernel 3 (rank_levels_kernel) gives every block its
+// exact rank in the (score, block id) order and the level that rank falls in;
+// kernel 4 (level_counts_kernel, one workgroup) counts the tokens of each
+// level, with each block's token count in closed form from the grid.
 //
 // Grid mapping of kernel 1: workgroups are renumbered XCD-aware and waves are
 // ordered column chunk fastest, then strip, then frame chunk, so the waves
@@ -43,10 +46,12 @@ namespace {
 
 constexpr int kAnalyzeWaves = 4;          // waves per workgroup of kernel 1
 constexpr int kXcds = 8;                  // accelerator dies (each with an L2) per GPU
-constexpr int kLevelsThreads = 1024;      // kernel 2 is one workgroup
-constexpr int kMaxBlocks = 16384;         // kernel 2 keeps all keys in LDS
+constexpr int kRankThreads = 1024;        // kernel 3 workgroup size
+constexpr int kRankSplit = 32;            // kernel 3 threads per block (one per 16 bytes of a 512-byte row)
+constexpr int kCountThreads = 1024;       // kernel 4 is one workgroup
+constexpr int kMaxBlocks = 16384;         // kernel 3 keeps all scores in LDS (a multiple of 128)
 #ifndef JANO_ANALYZE_TARGET_WAVES
-#define JANO_ANALYZE_TARGET_WAVES 4096
+#define JANO_ANALYZE_TARGET_WAVES 2304    // about 1.1 x the waves one pass of the GPU holds
 #endif
 constexpr int kTargetWaves = JANO_ANALYZE_TARGET_WAVES;  // waves wanted in the grid
 
@@ -258,131 +263,12 @@ __device__ __forceinline__ int axis_tokens(int j, int per_block, int ntok) {
   return max(0, min((j + 1) * per_block, ntok) - j * per_block);
 }
 
-// Finds, for each of two target ranks, the 64-bit key (score bits, block id)
-// at that rank. keys[] holds the fp32 score bits (non-negative scores are
-// ordered like their bit patterns). Radix select, 8 bits per pass: build the
-// digit histogram of the candidates in LDS, then 512 threads scan the two
-// 256-bin histograms in parallel to find the digit holding each target.
-__device__ void select_two(const uint32_t *keys, int B, const int target[2], uint64_t thr[2],
-                           uint32_t (*hist)[256], uint32_t *sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave, wv = tid / kWave, nw = blockDim.x / kWave;
-  // sh[0..1] prefix, sh[2..3] remaining rank, sh[4..5] found id,
-  // sh[8..8+2*nw) per-wave scratch
-  uint32_t *wtot = sh + 8;
-  if (tid < 2) {
-    sh[tid] = 0u;
-    sh[2 + tid] = static_cast<uint32_t>(target[tid]);
-  }
-  __syncthreads();
-  uint32_t mask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 2 * 256; i += blockDim.x) hist[i / 256][i % 256] = 0u;
-    __syncthreads();
-    const uint32_t p0 = sh[0], p1 = sh[1];
-    for (int b0 = 0; b0 < B; b0 += blockDim.x) {
-      const int b = b0 + tid;
-      const uint32_t u = b < B ? keys[b] : 0u;
-      const uint32_t dgt = (u >> shift) & 255u;
-      // Scores cluster, so most candidates of a wave share one digit: the
-      // first candidate's digit is counted with one atomic for the whole
-      // wave, the others one by one.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bool cand = b < B && (u & mask) == (t == 0 ? p0 : p1);
-        const uint64_t cm = __ballot(cand);
-        if (cm) {
-          const int first = __ffsll(static_cast<long long>(cm)) - 1;
-          const uint32_t lead = __shfl(dgt, first, kWave);
-          const uint64_t same = __ballot(cand && dgt == lead);
-          if (lane == first) atomicAdd(&hist[t][lead], static_cast<uint32_t>(__popcll(same)));
-          if (cand && dgt != lead) atomicAdd(&hist[t][dgt], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    // threads 0..511: target t = tid / 256, bin = tid % 256 (4 waves per target)
-    uint32_t h = 0, incl = 0;
-    if (tid < 512) {
-      h = hist[tid / 256][tid % 256];
-      incl = wave_inclusive_scan(h);
-      if (lane == kWave - 1) wtot[wv] = incl;
-    }
-    __syncthreads();
-    if (tid < 512) {
-      const int t = tid / 256;
-      uint32_t before = 0;
-      for (int j = t * 4; j < wv; ++j) before += wtot[j];
-      const uint32_t excl = before + incl - h;
-      const uint32_t k = sh[2 + t];
-      if (h > 0 && excl <= k && k < excl + h) {
-        sh[t] |= static_cast<uint32_t>(tid % 256) << shift;
-        sh[6 + t] = k - excl;
-      }
-    }
-    mask |= 255u << shift;
-    __syncthreads();
-    if (tid < 2) sh[2 + tid] = sh[6 + tid];
-    __syncthreads();
-  }
-  // The target is the k-th (in id order) block whose bits equal the prefix.
-  // When that score is unique (the usual case) the block is found directly;
-  // otherwise an ordered scan over the block ids ranks the equal scores.
-  if (tid < 2) sh[4 + tid] = 0xFFFFFFFFu;
-  __syncthreads();
-  bool unique = true;
-  for (int t = 0; t < 2; ++t) unique = unique && hist[t][sh[t] & 255u] == 1u;
-  if (unique) {
-    for (int b = tid; b < B; b += blockDim.x) {
-      if (keys[b] == sh[0]) sh[4] = static_cast<uint32_t>(b);
-      if (keys[b] == sh[1]) sh[5] = static_cast<uint32_t>(b);
-    }
-    __syncthreads();
-    for (int t = 0; t < 2; ++t)
-      thr[t] = (static_cast<uint64_t>(sh[t]) << 32) | static_cast<uint64_t>(sh[4 + t]);
-    __syncthreads();
-    return;
-  }
-  uint32_t run0 = 0, run1 = 0;
-  for (int b0 = 0; b0 < B; b0 += blockDim.x) {
-    const int b = b0 + tid;
-    const uint32_t u = b < B ? keys[b] : 0u;
-    const bool e0 = b < B && u == sh[0];
-    const bool e1 = b < B && u == sh[1];
-    const uint64_t m0 = __ballot(e0), m1 = __ballot(e1);
-    __syncthreads();
-    if (lane == 0) {
-      wtot[wv] = __popcll(m0);
-      wtot[nw + wv] = __popcll(m1);
-    }
-    __syncthreads();
-    uint32_t before0 = run0, before1 = run1, tot0 = 0, tot1 = 0;
-    for (int j = 0; j < nw; ++j) {
-      if (j < wv) {
-        before0 += wtot[j];
-        before1 += wtot[nw + j];
-      }
-      tot0 += wtot[j];
-      tot1 += wtot[nw + j];
-    }
-    if (e0 && before0 + lanes_below(m0) == sh[2]) sh[4] = static_cast<uint32_t>(b);
-    if (e1 && before1 + lanes_below(m1) == sh[3]) sh[5] = static_cast<uint32_t>(b);
-    run0 += tot0;
-    run1 += tot1;
-  }
-  __syncthreads();
-  for (int t = 0; t < 2; ++t)
-    thr[t] = (static_cast<uint64_t>(sh[t]) << 32) | static_cast<uint64_t>(sh[4 + t]);
-  __syncthreads();
-}
-
 // Kernel 2: per-block score (fixed-order sum of the partials over channels
-// and strips, divided by the closed-form term count, rounded to fp32) and
-// per-block token count. One thread per block.
+// and strips, divided by the closed-form term count, rounded to fp32). One
+// thread per block.
 __global__ __launch_bounds__(256) void block_scores_kernel(const double *__restrict__ part,
                                                            AnalyzeGeom g,
-                                                           float *__restrict__ scores,
-                                                           int32_t *__restrict__ tokcnt) {
+                                                           float *__restrict__ scores) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= g.B) return;
   const int B = g.B, CG = g.C * g.G;
@@ -406,46 +292,97 @@ __global__ __launch_bounds__(256) void block_scores_kernel(const double *__restr
                         (g.W >= 2 ? axis_terms(w0, w1, g.W) * ef * eh : 0);
   const long long n = pos * (g.K - 2) * g.C;
   scores[b] = n > 0 ? static_cast<float>(t / static_cast<double>(n)) : 0.0f;
-  const int tpbF = g.bF / g.pF, tpbH = g.bH / g.pH, tpbW = g.bW / g.pW;
-  tokcnt[b] = axis_tokens(bf, tpbF, g.F / g.pF) * axis_tokens(bh, tpbH, g.H / g.pH) *
-              axis_tokens(bw, tpbW, g.W / g.pW);
 }
 
-// Kernel 3 (one workgroup): the two rank thresholds of the (score, block id)
-// order, the levels, and the token count of each level.
-__global__ __launch_bounds__(kLevelsThreads) void levels_kernel(const float *__restrict__ scores,
-                                                                const int32_t *__restrict__ tokcnt,
-                                                                int B, int nS, int nSM,
-                                                                uint8_t *__restrict__ levels,
-                                                                int32_t *__restrict__ counts) {
-  __shared__ uint32_t keys[kMaxBlocks];
-  __shared__ uint32_t hist[2][256];
-  __shared__ uint32_t sh[8 + 2 * (kLevelsThreads / kWave)];
-  __shared__ int tok[3];
+// Kernel 3: the level of every block from its exact rank in the (score,
+// block id) order -- the number of blocks with a smaller score, or an equal
+// score and a smaller id. kRankSplit = 32 threads count one block's rank; each
+// workgroup stages all score bits in LDS (scores are >= 0, so their fp32 bit
+// patterns order like the values), padded to whole rows of 128 with
+// 0xFFFFFFFF, which no score reaches. Lane p of a block's 32 reads scores
+// 4p .. 4p+3 of every 128-score row (together one contiguous 512-byte row, no
+// bank conflicts). Rows wholly below block b count "score <= s", rows above
+// count "score < s", and the row holding b compares ids element by element.
+// Integer counts make the result exact and independent of scheduling.
+__global__ __launch_bounds__(kRankThreads) void rank_levels_kernel(const float *__restrict__ scores,
+                                                                   int B, int nS, int nSM,
+                                                                   uint8_t *__restrict__ levels) {
+  __shared__ __attribute__((aligned(16))) uint32_t sc[kMaxBlocks];
   const int tid = threadIdx.x;
-  if (tid < 3) tok[tid] = 0;
-  for (int b = tid; b < B; b += blockDim.x) keys[b] = __float_as_uint(scores[b]);
-  __syncthreads();
-
-  uint64_t thr[2];
-  const int target[2] = {nS < B ? nS : 0, nSM < B ? nSM : 0};
-  select_two(keys, B, target, thr, hist, sh);
-  if (nS >= B) thr[0] = ~0ull;
-  if (nSM >= B) thr[1] = ~0ull;
-
-  uint32_t my[3] = {0, 0, 0};
-  for (int b = tid; b < B; b += blockDim.x) {
-    const uint64_t key = (static_cast<uint64_t>(keys[b]) << 32) | static_cast<uint64_t>(b);
-    const int lv = key < thr[0] ? 1 : (key < thr[1] ? 2 : 3);
-    levels[b] = static_cast<uint8_t>(lv);
-    my[lv - 1] += static_cast<uint32_t>(tokcnt[b]);
+  const int nrows = (B + 127) / 128;
+  // stage the score bits: eight independent loads in flight per thread
+  for (int i0 = tid; i0 < nrows * 128; i0 += 8 * kRankThreads) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kRankThreads;
+      v[u] = i < B ? __float_as_uint(scores[i]) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kRankThreads;
+      if (i < nrows * 128) sc[i] = v[u];
+    }
   }
+  __syncthreads();
+  const int b = blockIdx.x * (kRankThreads / kRankSplit) + tid / kRankSplit;
+  const int part = tid % kRankSplit;
+  int cnt = 0;
+  if (b < B) {
+    const uint32_t s = sc[b];
+    const int rb = b / 128;
+    const uint32_t *p = &sc[4 * part];
+    for (int r = 0; r < rb; ++r) {
+      const uint4 t = *reinterpret_cast<const uint4 *>(p + 128 * r);
+      cnt += (t.x <= s) + (t.y <= s) + (t.z <= s) + (t.w <= s);
+    }
+    {
+      const uint4 t = *reinterpret_cast<const uint4 *>(p + 128 * rb);
+      const int j = 128 * rb + 4 * part;
+      const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        cnt += j + e < b ? (tv[e] <= s) : (j + e > b ? (tv[e] < s) : 0);
+    }
+    for (int r = rb + 1; r < nrows; ++r) {
+      const uint4 t = *reinterpret_cast<const uint4 *>(p + 128 * r);
+      cnt += (t.x < s) + (t.y < s) + (t.z < s) + (t.w < s);
+    }
+  }
+#pragma unroll
+  for (int off = kRankSplit / 2; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, kWave);
+  if (b < B && part == 0) levels[b] = static_cast<uint8_t>(cnt < nS ? 1 : (cnt < nSM ? 2 : 3));
+}
+
+// Kernel 4 (one workgroup): tokens per level; a block holds the tokens of its
+// (possibly ragged) extent in the token grid.
+__global__ __launch_bounds__(kCountThreads) void level_counts_kernel(const uint8_t *__restrict__ levels,
+                                                                     AnalyzeGeom g,
+                                                                     int32_t *__restrict__ counts) {
+  __shared__ uint32_t part[3][kCountThreads / kWave];
+  const int tid = threadIdx.x;
+  const int tpbF = g.bF / g.pF, tpbH = g.bH / g.pH, tpbW = g.bW / g.pW;
+  const int Ft = g.F / g.pF, Ht = g.H / g.pH, Wt = g.W / g.pW;
+  uint32_t my[3] = {0u, 0u, 0u};
+  for (int b = tid; b < g.B; b += kCountThreads) {
+    const int bw = b % g.nBW, bh = (b / g.nBW) % g.nBH, bf = b / (g.nBW * g.nBH);
+    const uint32_t tok = static_cast<uint32_t>(axis_tokens(bf, tpbF, Ft) * axis_tokens(bh, tpbH, Ht) *
+                                               axis_tokens(bw, tpbW, Wt));
+    const int lv = levels[b];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) my[i] += lv == i + 1 ? tok : 0u;
+  }
+#pragma unroll
   for (int i = 0; i < 3; ++i) {
     const uint32_t wsum = __shfl(wave_inclusive_scan(my[i]), kWave - 1, kWave);
-    if (tid % kWave == 0 && wsum) atomicAdd(&tok[i], static_cast<int>(wsum));
+    if (tid % kWave == 0) part[i][tid / kWave] = wsum;
   }
   __syncthreads();
-  if (tid < 3) counts[tid] = tok[tid];
+  if (tid < 3) {
+    uint32_t t = 0;
+    for (int w = 0; w < kCountThreads / kWave; ++w) t += part[tid][w];
+    counts[tid] = static_cast<int32_t>(t);
+  }
 }
 
 template <int KT, int R>
@@ -503,12 +440,12 @@ bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int
 }
 
 size_t analyze_ws_bytes(const AnalyzeGeom &g) {
-  // fp64 partials [C*G][B], then int32 token counts [B]
-  return static_cast<size_t>(g.C) * g.G * g.B * sizeof(double) + static_cast<size_t>(g.B) * 4;
+  // fp64 partials [C*G][B]
+  return static_cast<size_t>(g.C) * g.G * g.B * sizeof(double);
 }
 
-hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nSM, float *scores,
-                          uint8_t *levels, int32_t *counts, void *ws, hipStream_t s) {
+hipError_t launch_analyze_scores(const float *lat, const AnalyzeGeom &g, float *scores, void *ws,
+                                 hipStream_t s) {
   double *part = static_cast<double *>(ws);
   hipError_t e = hipSuccess;
   if (g.fast) {
@@ -527,13 +464,18 @@ hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nS
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  int32_t *tokcnt = reinterpret_cast<int32_t *>(part + static_cast<size_t>(g.C) * g.G * g.B);
-  hipLaunchKernelGGL(block_scores_kernel, dim3((g.B + 255) / 256), dim3(256), 0, s, part, g, scores,
-                     tokcnt);
-  e = hipGetLastError();
+  hipLaunchKernelGGL(block_scores_kernel, dim3((g.B + 255) / 256), dim3(256), 0, s, part, g, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_levels(const float *scores, const AnalyzeGeom &g, int nS, int nSM, uint8_t *levels,
+                         int32_t *counts, hipStream_t s) {
+  constexpr int per_wg = kRankThreads / kRankSplit;
+  hipLaunchKernelGGL(rank_levels_kernel, dim3((g.B + per_wg - 1) / per_wg), dim3(kRankThreads), 0, s,
+                     scores, g.B, nS, nSM, levels);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(levels_kernel, dim3(1), dim3(kLevelsThreads), 0, s, scores, tokcnt, g.B, nS, nSM,
-                     levels, counts);
+  hipLaunchKernelGGL(level_counts_kernel, dim3(1), dim3(kCountThreads), 0, s, levels, g, counts);
   return hipGetLastError();
 }
 

@@ -30,6 +30,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int hip_status(hipError_t e) { return e == hipSuccess ? JANO_OK : JANO_E_HIP; }
 
+bool mix_ok(int static_permille, int moderate_permille) {
+  return static_permille >= 0 && moderate_permille >= 0 && static_permille + moderate_permille <= 1000;
+}
+
+// rank thresholds of the level split: ranks < nS are Static, < nSM Moderate
+void split_ranks(int B, int static_permille, int moderate_permille, int *nS, int *nSM) {
+  const long long b = B;
+  *nS = static_cast<int>((static_permille * b + 500) / 1000);
+  *nSM = static_cast<int>(((static_permille + moderate_permille) * b + 500) / 1000);
+}
+
 void due_flags(const jano_sched *sc, int step, int due[3]) {
   const bool dense = step < sc->W || step >= sc->T - sc->Cd;
   for (int i = 0; i < 3; ++i) due[i] = dense || ((step - sc->W) % sc->period[i] == 0);
@@ -81,20 +92,38 @@ size_t jano_analyze_workspace_bytes(const jano_grid *g) {
   return jano::analyze_ws_bytes(a);
 }
 
+int jano_analyze_scores(const float *lat, const jano_grid *g, float *scores, void *ws,
+                        size_t ws_bytes, void *stream) {
+  if (!lat || !scores) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a)) return JANO_E_INVAL;
+  if (!ws || ws_bytes < jano::analyze_ws_bytes(a)) return JANO_E_WORKSPACE;
+  return hip_status(jano::launch_analyze_scores(lat, a, scores, ws, static_cast<hipStream_t>(stream)));
+}
+
+int jano_levels(const float *scores, const jano_grid *g, int static_permille, int moderate_permille,
+                uint8_t *levels, int32_t *level_tok_counts, void *stream) {
+  if (!scores || !levels || !level_tok_counts) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a) || !mix_ok(static_permille, moderate_permille)) return JANO_E_INVAL;
+  int nS, nSM;
+  split_ranks(a.B, static_permille, moderate_permille, &nS, &nSM);
+  return hip_status(jano::launch_levels(scores, a, nS, nSM, levels, level_tok_counts,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int jano_analyze(const float *lat, const jano_grid *g, int static_permille, int moderate_permille,
                  float *scores, uint8_t *levels, int32_t *level_tok_counts, void *ws,
                  size_t ws_bytes, void *stream) {
   if (!lat || !scores || !levels || !level_tok_counts) return JANO_E_INVAL;
   AnalyzeGeom a;
-  if (!grid_ok(g, &a)) return JANO_E_INVAL;
-  if (static_permille < 0 || moderate_permille < 0 || static_permille + moderate_permille > 1000)
-    return JANO_E_INVAL;
+  if (!grid_ok(g, &a) || !mix_ok(static_permille, moderate_permille)) return JANO_E_INVAL;
   if (!ws || ws_bytes < jano::analyze_ws_bytes(a)) return JANO_E_WORKSPACE;
-  const long long B = a.B;
-  const int nS = static_cast<int>((static_permille * B + 500) / 1000);
-  const int nSM = static_cast<int>(((static_permille + moderate_permille) * B + 500) / 1000);
-  return hip_status(jano::launch_analyze(lat, a, nS, nSM, scores, levels, level_tok_counts, ws,
-                                         static_cast<hipStream_t>(stream)));
+  int nS, nSM;
+  split_ranks(a.B, static_permille, moderate_permille, &nS, &nSM);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jano::launch_analyze_scores(lat, a, scores, ws, s) != hipSuccess) return JANO_E_HIP;
+  return hip_status(jano::launch_levels(scores, a, nS, nSM, levels, level_tok_counts, s));
 }
 
 int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *sc, int step,

@@ -28,9 +28,12 @@ struct AnalyzeGeom {
 bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int pF,
                   int pH, int pW, AnalyzeGeom *g);
 size_t analyze_ws_bytes(const AnalyzeGeom &g);
-hipError_t launch_analyze(const float *lat, const AnalyzeGeom &g, int nS, int nSM,
-                          float *scores, uint8_t *levels, int32_t *counts, void *ws,
-                          hipStream_t s);
+// jano_analyze_scores: kernels 1 and 2 (scores [B]; ws holds the partials)
+hipError_t launch_analyze_scores(const float *lat, const AnalyzeGeom &g, float *scores, void *ws,
+                                 hipStream_t s);
+// jano_levels: kernels 3 and 4 (levels [B], tokens per level [3])
+hipError_t launch_levels(const float *scores, const AnalyzeGeom &g, int nS, int nSM, uint8_t *levels,
+                         int32_t *counts, hipStream_t s);
 
 struct SchedGeom {
   int Ft, Ht, Wt;         // token grid

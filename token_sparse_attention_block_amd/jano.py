@@ -19,7 +19,8 @@ JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_
 
 EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
-    "jano_analyze_workspace_bytes", "jano_analyze", "jano_schedule", "jano_gather_rows",
+    "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_levels", "jano_analyze",
+    "jano_schedule", "jano_gather_rows",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
 )
 
@@ -78,6 +79,8 @@ def lib():
             "jano_grid_sizes": ([gp, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
             "jano_schedule_count": ([ctypes.POINTER(ctypes.c_int32), sp, i32, ctypes.POINTER(i64)], i32),
             "jano_analyze_workspace_bytes": ([gp], ctypes.c_size_t),
+            "jano_analyze_scores": ([vp, gp, vp, vp, ctypes.c_size_t, vp], i32),
+            "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
             "jano_analyze": ([vp, gp, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
             "jano_schedule": ([vp, gp, sp, i32, vp, vp, vp], i32),
             "jano_gather_rows": ([vp, i64, i64, vp, i64, vp, vp], i32),
@@ -180,6 +183,44 @@ def analyze(lat, spec: GridSpec, static_permille=400, moderate_permille=300,
         _ptr(lat), ctypes.byref(g), int(static_permille), int(moderate_permille), _ptr(scores),
         _ptr(levels), _ptr(counts), _ptr(workspace), workspace.numel(), _stream(lat)))
     return scores, levels, counts
+
+
+def analyze_scores(lat, spec: GridSpec, scores=None, workspace=None):
+    """jano_analyze_scores. lat fp32 [K,C,F,H,W] on device -> scores fp32 [B]
+    on the device."""
+    torch = _torch()
+    _need(lat, "lat", torch.float32, (spec.K, spec.C, spec.F, spec.H, spec.W))
+    B, _ = grid_sizes(spec)
+    dev = lat.device
+    scores = torch.empty(B, dtype=torch.float32, device=dev) if scores is None else scores
+    _need(scores, "scores", torch.float32, (B,), dev)
+    nbytes = analyze_workspace_bytes(spec)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    g = spec.c()
+    _check("jano_analyze_scores", lib().jano_analyze_scores(
+        _ptr(lat), ctypes.byref(g), _ptr(scores), _ptr(workspace), workspace.numel(), _stream(lat)))
+    return scores
+
+
+def levels(scores, spec: GridSpec, static_permille=400, moderate_permille=300, levels=None,
+           counts=None):
+    """jano_levels. scores fp32 [B] on device -> (levels uint8 [B],
+    counts int32 [3]) on the device."""
+    torch = _torch()
+    B, _ = grid_sizes(spec)
+    _need(scores, "scores", torch.float32, (B,))
+    dev = scores.device
+    lv = torch.empty(B, dtype=torch.uint8, device=dev) if levels is None else levels
+    counts = torch.empty(3, dtype=torch.int32, device=dev) if counts is None else counts
+    _need(lv, "levels", torch.uint8, (B,), dev)
+    _need(counts, "counts", torch.int32, (3,), dev)
+    g = spec.c()
+    _check("jano_levels", lib().jano_levels(
+        _ptr(scores), ctypes.byref(g), int(static_permille), int(moderate_permille), _ptr(lv),
+        _ptr(counts), _stream(scores)))
+    return lv, counts
 
 
 def schedule(levels, spec: GridSpec, step, T=50, W=5, Cd=5, periods=(4, 2, 1), idx=None, n_act=None):
