@@ -283,3 +283,28 @@ def attn_step(Q_act_bits, Knew_bits, Vnew_bits, idx, Kc_bits, Vc_bits, scale=Non
         Q = Q[np.asarray(queries)]
     out = attention(Q, bf16_to_f64(Kc2), bf16_to_f64(Vc2), scale, dtype=dtype)
     return out, Kc2, Vc2
+
+
+# --------------------------------------------------------------------------
+# Write-back of the active tokens' model output and the sampler step.
+# Jano pages: [nl] "three groups" (the static group rests and its result is
+# remembered); [zh] three classes (static regions skip intermediate steps and
+# use the cache instead); [ko] §2 (skipped parts keep using the previous state
+# held in memory). Reading taken: every token keeps its latest model output in
+# a full-sequence buffer; active tokens overwrite theirs, frozen tokens reuse
+# theirs, and every token takes the sampler step with that output.
+# --------------------------------------------------------------------------
+
+def writeback_step(out_act_bits, idx, out_full_bits, x, dt):
+    """Returns (out_full', x').
+
+    out_act_bits [n_act, P] bf16 bits: the fresh model output of the active
+    tokens idx; out_full_bits [N, P] bf16 bits: every token's latest output;
+    x [N, P] fp32 sampler state (token-major latent patches). The active rows
+    of out_full are replaced, then x' = x + dt * out_full' elementwise (one
+    Euler step), evaluated exactly in fp64 (a bf16 x fp32 product is exact, and
+    the sum is correctly rounded) and rounded once to fp32."""
+    of = scatter_rows(out_full_bits, idx, out_act_bits)
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    x2 = x64 + np.float64(np.float32(dt)) * bf16_to_f64(of)
+    return of, x2.astype(np.float32)

@@ -335,3 +335,65 @@ def test_bf16_decode():
     assert v[0] == 1.0 and v[1] == -1.0 and v[2] == 0.0 and np.isinf(v[3])
     assert v[4] == 3.140625
     assert v[5] == 2.0 ** -133
+
+
+# ---------------------------------------------------------------- write-back
+
+def _wb_inputs(N=12, P=5, seed=3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, P)).astype(np.float32)
+    full = rng.integers(0x3C00, 0x4100, size=(N, P), dtype=np.uint16)
+    return rng, x, full
+
+
+def test_writeback_closed_forms():
+    # x = 1, out = 2 (bf16 0x4000), dt = 0.25 -> x' = 1.5 exactly; frozen rows
+    # keep their cached output and step with it (out = -0.5, bf16 0xBF00)
+    x = np.ones((3, 2), np.float32)
+    full = np.full((3, 2), 0xBF00, np.uint16)
+    act = np.full((1, 2), 0x4000, np.uint16)
+    of, x2 = O.writeback_step(act, np.array([1]), full, x, 0.25)
+    assert of[1].tolist() == [0x4000, 0x4000] and of[0].tolist() == [0xBF00, 0xBF00]
+    assert x2[1].tolist() == [1.5, 1.5]
+    assert x2[0].tolist() == [0.875, 0.875] and x2[2].tolist() == [0.875, 0.875]
+
+
+def test_writeback_dt_zero_and_empty():
+    rng, x, full = _wb_inputs()
+    act = rng.integers(0, 0x7F00, size=(4, 5), dtype=np.uint16)
+    idx = np.array([0, 3, 4, 11])
+    of, x2 = O.writeback_step(act, idx, full, x, 0.0)
+    np.testing.assert_array_equal(x2.view(np.uint32), x.view(np.uint32))
+    np.testing.assert_array_equal(of[idx], act)
+    keep = np.setdiff1d(np.arange(12), idx)
+    np.testing.assert_array_equal(of[keep], full[keep])
+    of, x3 = O.writeback_step(np.zeros((0, 5), np.uint16), np.zeros(0, np.int64), full, x, -0.1)
+    np.testing.assert_array_equal(of, full)
+
+
+def test_writeback_bruteforce_all_active():
+    # every token active: scalar loops with Python floats (fp64) rounded once
+    rng, x, full = _wb_inputs(N=4, P=3, seed=9)
+    act = rng.integers(0x3000, 0x4400, size=(4, 3), dtype=np.uint16)
+    perm = np.array([2, 0, 3, 1])
+    dt = np.float32(-0.0625)
+    of, x2 = O.writeback_step(act, perm, full, x, dt)
+    for i in range(4):
+        for p in range(3):
+            v = float(np.array([int(act[i, p]) << 16], np.uint32).view(np.float32)[0])
+            want = np.float32(float(x[perm[i], p]) + float(dt) * v)
+            assert of[perm[i], p] == act[i, p]
+            assert x2[perm[i], p] == want, (i, p)
+
+
+def test_writeback_two_steps_compose():
+    # stepping twice with the same active set = writing once, stepping twice
+    rng, x, full = _wb_inputs(seed=5)
+    act = rng.integers(0x3400, 0x4200, size=(5, 5), dtype=np.uint16)
+    idx = np.array([1, 2, 6, 7, 9])
+    of1, x1 = O.writeback_step(act, idx, full, x, 0.5)
+    of2, x2 = O.writeback_step(act, idx, of1, x1, 0.5)
+    np.testing.assert_array_equal(of2, of1)
+    step = np.float64(0.5) * O.bf16_to_f64(of1)
+    want = ((x.astype(np.float64) + step).astype(np.float32).astype(np.float64) + step).astype(np.float32)
+    np.testing.assert_array_equal(x2, want)
