@@ -232,6 +232,31 @@ def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup)
     return p, n, wall * 1e3, per
 
 
+def time_writeback(torch, jano, cfg, idx, reps=20):
+    """jano_writeback_step on the token outputs of the workload: P = C * patch
+    values per token, fresh rows for the active tokens, fp32 sampler state."""
+    P = cfg.C * cfg.patch[0] * cfg.patch[1] * cfg.patch[2]
+    N, n = cfg.N, idx.numel()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    out_full = torch.randn((N, P), generator=g, device="cuda").to(torch.bfloat16)
+    out_act = torch.randn((n, P), generator=g, device="cuda").to(torch.bfloat16)
+    x = torch.randn((N, P), generator=g, device="cuda")
+    for _ in range(3):
+        jano.writeback_step(out_act, idx, out_full, x, -0.02)
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(reps):
+        jano.writeback_step(out_act, idx, out_full, x, -0.02)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 2 * n * P * 2 + N * P * (2 + 4 + 4)
+    return {"ms": round(ms, 5), "tokens": N, "values_per_token": P, "n_act": n, "bytes": nbytes,
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 3),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5)}
+
+
 def time_dense(torch, jano, Q, Kc, Vc, reps):
     out = torch.empty_like(Q)
     jano.attention(Q, Kc, Vc, out=out)
@@ -397,6 +422,9 @@ def main():
             if isinstance(v[kk], float):
                 v[kk] = round(v[kk], 5)
 
+    print("bench: write-back step", file=sys.stderr, flush=True)
+    writeback = time_writeback(torch, jano, cfg, p.idx[:n_act])
+
     print("bench: dense reference", file=sys.stderr, flush=True)
     dense_ms = time_dense(torch, jano, Q, Kc, Vc, 3)
     dense_tflops = 4.0 * N * N * H * d / (dense_ms * 1e-3) / 1e12
@@ -452,6 +480,7 @@ def main():
         "step_speedup_vs_dense": speedups,
         "dense": {"ms": round(dense_ms, 4), "TFLOP/s": round(dense_tflops, 3)},
         "kernels": kernels,
+        "writeback": writeback,
     }
     line.update(extra)
     print(json.dumps(line), flush=True)

@@ -191,6 +191,27 @@ int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t 
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
 
 /*
+ * jano_writeback_step -- write the active tokens' model output back and take
+ * one sampler (Euler) step for every token.
+ * Pages: nl "three groups" (the static group rests while its result is
+ * remembered); zh three token classes (static regions skip intermediate steps
+ * and use the cache instead); ko §2 (skipped parts keep the previous state
+ * held in memory). Every token keeps its latest model output; frozen tokens
+ * step with the output cached at their last update.
+ *   out_act  [n_act][P] bf16: fresh model output of the tokens idx
+ *   idx      [n_act] distinct indices in [0, N) (from jano_schedule)
+ *   out_full [N][P] bf16, in/out: every token's latest output; rows idx are
+ *            replaced by out_act
+ *   x        [N][P] fp32, in/out: sampler state in token-major patch layout;
+ *            x = fma(dt, out_full, x) elementwise after the write-back
+ *   dt       finite step size (the sampler's signed time increment)
+ * n_act == 0 only steps x. Duplicate indices race.
+ */
+int jano_writeback_step(const uint16_t *out_act, const int32_t *idx, int64_t n_act,
+                        uint16_t *out_full, float *x, int64_t N, int64_t P, float dt,
+                        void *stream);
+
+/*
  * jano_check_idx -- validate an index list on the device: writes 0 to
  * *flag_dev when idx is strictly ascending within [0, N), else JANO_E_RANGE.
  * Debug aid for the precondition of jano_scatter_kv / jano_attn_step.

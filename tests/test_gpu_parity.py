@@ -225,6 +225,54 @@ def test_analyze_scores_entry_point(torch):
     np.testing.assert_array_equal(s2.cpu().numpy(), s1.cpu().numpy())
 
 
+# ------------------------------------------------------------------ write-back
+
+def _wb_case(rng, N, P, n_act):
+    x = rng.standard_normal((N, P)).astype(np.float32)
+    full = synth.f32_to_bf16_bits(rng.standard_normal((N, P)).astype(np.float32))
+    act = synth.f32_to_bf16_bits(rng.standard_normal((n_act, P)).astype(np.float32))
+    idx = np.sort(rng.choice(N, size=n_act, replace=False)).astype(np.int32)
+    return x, full, act, idx
+
+
+def _wb_check(torch, x, full, act, idx, dt, x_off=0):
+    N, P = full.shape
+    ref_full, ref_x = O.writeback_step(act, idx, full, x, dt)
+    of = dev_bf16(full)
+    # x_off > 0 places x at an element offset, so the vector path is not aligned
+    xbuf = torch.zeros(N * P + x_off, dtype=torch.float32, device="cuda")
+    xd = xbuf[x_off:].view(N, P)
+    xd.copy_(torch.from_numpy(x).cuda())
+    jano.writeback_step(dev_bf16(act) if len(idx) else dev_bf16(np.zeros((1, P), np.uint16)),
+                        dev(idx) if len(idx) else dev(np.zeros(1, np.int32)), of, xd, dt,
+                        n_act=len(idx))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(of), ref_full)
+    np.testing.assert_array_equal(xd.cpu().numpy().view(np.uint32), ref_x.view(np.uint32))
+
+
+@pytest.mark.parametrize("cfg,frac", [(configs.TINY, 0.3), (configs.IMAGE, 0.3), (configs.V720, 0.25)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_writeback_bit_exact(torch, cfg, frac):
+    print("writeback", cfg.name, frac, flush=True)
+    rng = np.random.default_rng(cfg.cfg_id)
+    P = cfg.C * cfg.patch[0] * cfg.patch[1] * cfg.patch[2]
+    idx = _idx_for(cfg, frac)
+    x, full, act, _ = _wb_case(rng, cfg.N, P, len(idx))
+    _wb_check(torch, x, full, act, idx, -0.02)
+
+
+def test_writeback_edges(torch):
+    rng = np.random.default_rng(11)
+    x, full, act, idx = _wb_case(rng, 37, 5, 9)        # 185 elements: vector body + tail
+    _wb_check(torch, x, full, act, idx, 0.125)
+    _wb_check(torch, x, full, act, idx, 0.125, x_off=1)  # unaligned: scalar path
+    x, full, act, idx = _wb_case(rng, 16, 8, 0)         # nothing active: x still steps
+    _wb_check(torch, x, full, act, idx, -1.0)
+    x, full, act, idx = _wb_case(rng, 16, 8, 16)        # everything active
+    _wb_check(torch, x, full, act, idx, 0.0)
+
+
 # ------------------------------------------------------------------ schedule
 
 def test_schedule_all_steps_480p(torch):

@@ -2,6 +2,7 @@
 // Every check happens before anything is enqueued, so a non-zero return
 // means nothing ran and no output was touched.
 #include <math.h>
+#include <stdint.h>
 
 #include "../../include/jano.h"
 #include "kernels.hpp"
@@ -197,6 +198,17 @@ int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t 
   if (e != hipSuccess) return JANO_E_HIP;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
   return hip_status(jano::launch_attention(Q_act, n_act, Kc, Vc, N, H, d, sc, out, s));
+}
+
+int jano_writeback_step(const uint16_t *out_act, const int32_t *idx, int64_t n_act,
+                        uint16_t *out_full, float *x, int64_t N, int64_t P, float dt, void *stream) {
+  if (N < 1 || P < 1 || n_act < 0 || n_act > N || N > kMaxRows || !isfinite(dt)) return JANO_E_INVAL;
+  if (N > INT64_MAX / P) return JANO_E_INVAL;
+  if (!out_full || !x) return JANO_E_INVAL;
+  if (n_act > 0 && (!out_act || !idx)) return JANO_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jano::launch_scatter_rows(out_act, P, idx, n_act, out_full, s) != hipSuccess) return JANO_E_HIP;
+  return hip_status(jano::launch_euler(out_full, x, N * P, dt, s));
 }
 
 int jano_check_idx(const int32_t *idx, int64_t n_act, int64_t N, int32_t *flag_dev, void *stream) {

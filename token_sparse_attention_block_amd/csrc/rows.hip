@@ -1,4 +1,5 @@
-// Row gather (adaptive token activation) and KV-cache row scatter (gfx950).
+// Row gather (adaptive token activation), KV-cache row scatter, and the
+// write-back + sampler step of the token outputs (gfx950).
 //
 // Method (Jano pages, nl methodology §2 and contributions item 2; zh §2.2
 // item 3): only the tokens due at a step are computed, and the key/value pairs
@@ -6,7 +7,14 @@
 // tokens are written into a persistent full-sequence cache at their token
 // positions, so the cache always holds every token's latest K/V.
 //
-// Both kernels are pure HBM streams: one workgroup per row, sized to the row
+// Write-back (Jano pages, nl "three groups": the static group rests and its
+// result is remembered; zh: static regions use the cache instead; ko §2:
+// skipped parts keep the previous state in memory): the fresh model output of
+// the active tokens replaces their rows of a full-sequence output buffer, and
+// every token takes one Euler step x += dt * out with its latest output, so
+// frozen tokens advance with the output cached at their last update.
+//
+// All kernels are pure HBM streams: one workgroup per row, sized to the row
 // (one 16-byte dwordx4 chunk per thread up to 1024 threads, so a 10 KB row of
 // 40 heads x 128 dims is copied by 640 threads in a single pass), rows of H*d
 // bf16. A scalar path covers rows whose byte size or base addresses are not
@@ -72,6 +80,83 @@ __global__ __launch_bounds__(kRowThreads) void scatter_kv_u16(const uint16_t *__
   for (long long c = threadIdx.x; c < D; c += kRowThreads) d[drow * D + c] = s[row * D + c];
 }
 
+// single-tensor row scatter: dst[idx[row]] = src[row]
+__global__ __launch_bounds__(kMaxRowThreads) void scatter_rows_v16(const u32x4 *__restrict__ src,
+                                                                const int32_t *__restrict__ idx,
+                                                                u32x4 *__restrict__ dst, int chunks) {
+  const long long row = blockIdx.x;
+  const long long drow = idx[row];
+  const u32x4 *s = src + row * chunks;
+  u32x4 *d = dst + drow * chunks;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+}
+
+// rows of at most 32 chunks: several rows per workgroup, one thread per chunk
+constexpr int kSmallRowThreads = 256;
+__global__ __launch_bounds__(kSmallRowThreads) void scatter_rows_small_v16(const u32x4 *__restrict__ src,
+                                                                       const int32_t *__restrict__ idx,
+                                                                       u32x4 *__restrict__ dst,
+                                                                       int chunks, long long n) {
+  const int rows_per_wg = kSmallRowThreads / chunks;
+  const int t = threadIdx.x;
+  if (t >= rows_per_wg * chunks) return;
+  const long long row = static_cast<long long>(blockIdx.x) * rows_per_wg + t / chunks;
+  if (row >= n) return;
+  const int c = t % chunks;
+  const long long drow = idx[row];
+  __builtin_nontemporal_store(__builtin_nontemporal_load(src + row * chunks + c), dst + drow * chunks + c);
+}
+
+__global__ __launch_bounds__(kRowThreads) void scatter_rows_u16(const uint16_t *__restrict__ src,
+                                                                const int32_t *__restrict__ idx,
+                                                                uint16_t *__restrict__ dst,
+                                                                long long D) {
+  const long long row = blockIdx.x;
+  const long long drow = idx[row];
+  for (long long c = threadIdx.x; c < D; c += kRowThreads) dst[drow * D + c] = src[row * D + c];
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+constexpr int kEulerThreads = 256;
+constexpr int kEulerMaxBlocks = 8192;
+
+// x[e] = fma(dt, v[e], x[e]) over a flat array, 8 elements per thread and step
+__global__ __launch_bounds__(kEulerThreads) void euler_v8(const u32x4 *__restrict__ v,
+                                                          f32x4 *__restrict__ x, long long n8,
+                                                          float dt) {
+  for (long long i = static_cast<long long>(blockIdx.x) * kEulerThreads + threadIdx.x; i < n8;
+       i += static_cast<long long>(gridDim.x) * kEulerThreads) {
+    const u32x4 w = __builtin_nontemporal_load(v + i);
+    f32x4 a = x[2 * i], b = x[2 * i + 1];
+    a.x = fmaf(dt, bf16_lo(w.x), a.x);
+    a.y = fmaf(dt, bf16_hi(w.x), a.y);
+    a.z = fmaf(dt, bf16_lo(w.y), a.z);
+    a.w = fmaf(dt, bf16_hi(w.y), a.w);
+    b.x = fmaf(dt, bf16_lo(w.z), b.x);
+    b.y = fmaf(dt, bf16_hi(w.z), b.y);
+    b.z = fmaf(dt, bf16_lo(w.w), b.z);
+    b.w = fmaf(dt, bf16_hi(w.w), b.w);
+    __builtin_nontemporal_store(a, x + 2 * i);
+    __builtin_nontemporal_store(b, x + 2 * i + 1);
+  }
+}
+
+__global__ __launch_bounds__(kEulerThreads) void euler_scalar(const uint16_t *__restrict__ v,
+                                                              float *__restrict__ x, long long lo,
+                                                              long long hi, float dt) {
+  for (long long e = lo + static_cast<long long>(blockIdx.x) * kEulerThreads + threadIdx.x; e < hi;
+       e += static_cast<long long>(gridDim.x) * kEulerThreads)
+    x[e] = fmaf(dt, __uint_as_float(static_cast<uint32_t>(v[e]) << 16), x[e]);
+}
+
+int euler_blocks(long long work) {
+  const long long b = (work + kEulerThreads - 1) / kEulerThreads;
+  return static_cast<int>(b < 1 ? 1 : (b > kEulerMaxBlocks ? kEulerMaxBlocks : b));
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -103,6 +188,42 @@ hipError_t launch_scatter_kv(const uint16_t *Kn, const uint16_t *Vn, const int32
     hipLaunchKernelGGL(scatter_kv_u16, dim3(static_cast<unsigned>(n), 2), dim3(kRowThreads), 0, s,
                        Kn, Vn, idx, Kc, Vc, static_cast<long long>(HD));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const uint16_t *src, int64_t D, const int32_t *idx, int64_t n,
+                               uint16_t *dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if ((D * 2) % 16 == 0 && aligned16(src) && aligned16(dst)) {
+    const int chunks = static_cast<int>(D * 2 / 16);
+    if (chunks <= 32) {
+      const long long per = kSmallRowThreads / chunks;
+      hipLaunchKernelGGL(scatter_rows_small_v16, dim3(static_cast<unsigned>((n + per - 1) / per)),
+                         dim3(kSmallRowThreads), 0, s, reinterpret_cast<const u32x4 *>(src), idx,
+                         reinterpret_cast<u32x4 *>(dst), chunks, static_cast<long long>(n));
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(scatter_rows_v16, dim3(static_cast<unsigned>(n)), dim3(row_threads(chunks)), 0, s,
+                       reinterpret_cast<const u32x4 *>(src), idx, reinterpret_cast<u32x4 *>(dst), chunks);
+  } else {
+    hipLaunchKernelGGL(scatter_rows_u16, dim3(static_cast<unsigned>(n)), dim3(kRowThreads), 0, s, src,
+                       idx, dst, static_cast<long long>(D));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_euler(const uint16_t *v, float *x, int64_t total, float dt, hipStream_t s) {
+  long long done = 0;
+  if (aligned16(v) && aligned16(x)) {
+    const long long n8 = total / 8;
+    if (n8 > 0)
+      hipLaunchKernelGGL(euler_v8, dim3(euler_blocks(n8)), dim3(kEulerThreads), 0, s,
+                         reinterpret_cast<const u32x4 *>(v), reinterpret_cast<f32x4 *>(x), n8, dt);
+    done = n8 * 8;
+  }
+  if (done < total)
+    hipLaunchKernelGGL(euler_scalar, dim3(euler_blocks(total - done)), dim3(kEulerThreads), 0, s, v, x,
+                       done, static_cast<long long>(total), dt);
   return hipGetLastError();
 }
 

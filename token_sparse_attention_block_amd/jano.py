@@ -20,7 +20,7 @@ JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_
 EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
     "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_levels", "jano_analyze",
-    "jano_schedule", "jano_gather_rows",
+    "jano_schedule", "jano_gather_rows", "jano_writeback_step",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
 )
 
@@ -79,6 +79,7 @@ def lib():
             "jano_grid_sizes": ([gp, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
             "jano_schedule_count": ([ctypes.POINTER(ctypes.c_int32), sp, i32, ctypes.POINTER(i64)], i32),
             "jano_analyze_workspace_bytes": ([gp], ctypes.c_size_t),
+            "jano_writeback_step": ([vp, vp, i64, vp, vp, i64, i64, ctypes.c_float, vp], i32),
             "jano_analyze_scores": ([vp, gp, vp, vp, ctypes.c_size_t, vp], i32),
             "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
             "jano_analyze": ([vp, gp, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
@@ -329,6 +330,26 @@ def attn_step(Q_act, K_new, V_new, idx, Kc, Vc, scale=0.0, out=None, n_act=None)
         _ptr(Q_act), _ptr(K_new), _ptr(V_new), _ptr(idx), n, _ptr(Kc), _ptr(Vc), N, H, d,
         float(scale), _ptr(out), _stream(Kc)))
     return out
+
+
+def writeback_step(out_act, idx, out_full, x, dt, n_act=None):
+    """jano_writeback_step: out_full[idx] = out_act (bf16 rows), then
+    x += dt * out_full for every token (x fp32 [N, P], updated in place)."""
+    torch = _torch()
+    _need(out_full, "out_full", torch.bfloat16)
+    if out_full.dim() != 2:
+        raise ValueError("out_full must be [N, P]")
+    N, P = out_full.shape
+    dev = out_full.device
+    _need(x, "x", torch.float32, (N, P), dev)
+    n = idx.numel() if n_act is None else int(n_act)
+    _need(idx, "idx", torch.int32, None, dev)
+    _need(out_act, "out_act", torch.bfloat16, None, dev)
+    if n > idx.numel() or out_act.dim() != 2 or out_act.shape[1] != P or out_act.shape[0] < n:
+        raise ValueError("out_act must be [>= n_act, P] and idx hold >= n_act entries")
+    _check("jano_writeback_step", lib().jano_writeback_step(
+        _ptr(out_act), _ptr(idx), n, _ptr(out_full), _ptr(x), N, P, float(dt), _stream(out_full)))
+    return out_full, x
 
 
 def check_idx(idx, N, n_act=None, flag=None):
