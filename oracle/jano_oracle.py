@@ -201,6 +201,12 @@ def schedule(tok_levels, step, T, W, Cd, periods=(4, 2, 1)) -> np.ndarray:
     return np.flatnonzero(active_mask(tok_levels, step, T, W, Cd, periods)).astype(np.int32)
 
 
+def schedule_frozen(tok_levels, step, T, W, Cd, periods=(4, 2, 1)) -> np.ndarray:
+    """Ascending int32 indices of the tokens NOT computed at this step (their
+    keys/values come from the cache)."""
+    return np.flatnonzero(~active_mask(tok_levels, step, T, W, Cd, periods)).astype(np.int32)
+
+
 # --------------------------------------------------------------------------
 # Token activation and the full-sequence KV cache. Jano pages: [nl]
 # methodology §2 (KV cache of frozen tokens; cached pairs combined with the
@@ -216,6 +222,13 @@ def scatter_rows(cache: np.ndarray, idx: np.ndarray, rows: np.ndarray) -> np.nda
     out = np.array(cache, copy=True)
     out[np.asarray(idx, dtype=np.int64)] = rows
     return out
+
+
+def concat_kv(Knew_bits, Kc_bits, frozen_idx) -> np.ndarray:
+    """The pages' layout of one interleaved step: the fresh rows of the active
+    tokens first, then the cached rows of the frozen tokens, positions not
+    restored ([nl] methodology §2; [fr] §2.B; [ko] KV-cache item)."""
+    return np.concatenate([np.asarray(Knew_bits), np.asarray(Kc_bits)[np.asarray(frozen_idx, np.int64)]])
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -397,3 +397,34 @@ def test_writeback_two_steps_compose():
     step = np.float64(0.5) * O.bf16_to_f64(of1)
     want = ((x.astype(np.float64) + step).astype(np.float32).astype(np.float64) + step).astype(np.float32)
     np.testing.assert_array_equal(x2, want)
+
+
+# ------------------------------------------------------- concatenated layout
+
+def test_schedule_frozen_is_the_complement():
+    cfg = configs.TINY
+    lv = synth.active_level_map(cfg, 0.3)
+    tl = O.token_levels(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    sc = cfg.schedule
+    for step in range(sc.T):
+        act = O.schedule(tl, step, sc.T, sc.W, sc.Cd, sc.periods)
+        frz = O.schedule_frozen(tl, step, sc.T, sc.W, sc.Cd, sc.periods)
+        assert len(np.intersect1d(act, frz)) == 0
+        np.testing.assert_array_equal(np.union1d(act, frz), np.arange(cfg.N))
+        assert np.all(np.diff(frz) > 0)
+        if step < sc.W or step >= sc.T - sc.Cd:
+            assert len(frz) == 0
+
+
+def test_concat_layout_rows():
+    # row i < n_act is the fresh row i; row n_act + j is the cached row frozen[j]
+    rng = np.random.default_rng(4)
+    Kc = rng.integers(0, 65535, size=(9, 3), dtype=np.uint16)
+    Kn = rng.integers(0, 65535, size=(2, 3), dtype=np.uint16)
+    frozen = np.array([0, 3, 4, 8])
+    cat = O.concat_kv(Kn, Kc, frozen)
+    assert cat.shape == (6, 3)
+    for i in range(2):
+        assert cat[i].tolist() == Kn[i].tolist()
+    for j, r in enumerate(frozen):
+        assert cat[2 + j].tolist() == Kc[r].tolist()
