@@ -257,6 +257,43 @@ def time_writeback(torch, jano, cfg, idx, reps=20):
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5)}
 
 
+def time_concat_layout(torch, jano, p, Q, K, V, reps=3):
+    """The pages' own layout of an interleaved step, [fresh K/V of the active
+    tokens ; cached K/V of the frozen tokens], timed beside the scatter cache:
+    frozen-token list, concatenation, attention over the concatenated K/V."""
+    n = p.n_act
+    T, W, Cd, per = p.sched
+    idx = p.idx[:n]
+    fidx, nf_dev = jano.schedule(p.levels, p.spec, p.step_id, T, W, Cd, per, frozen=True)
+    torch.cuda.synchronize()
+    nf = int(nf_dev.item())
+    Kn, Vn = jano.gather_rows(K, idx, n), jano.gather_rows(V, idx, n)
+    q_act = jano.gather_rows(Q, idx, n)
+    Kcat = torch.empty((n + nf,) + tuple(K.shape[1:]), dtype=torch.bfloat16, device="cuda")
+    Vcat = torch.empty_like(Kcat)
+    out = torch.empty_like(q_act)
+    calls = (lambda: jano.schedule(p.levels, p.spec, p.step_id, T, W, Cd, per, idx=fidx, n_act=nf_dev,
+                                   frozen=True),
+             lambda: jano.concat_kv(Kn, Vn, K, V, fidx, n_act=n, n_frozen=nf, Kcat=Kcat, Vcat=Vcat),
+             lambda: jano.attention(q_act, Kcat, Vcat, out=out, n_q=n))
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ev = [[_ev(torch) for _ in range(len(calls) + 1)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        for j, c in enumerate(calls):
+            c()
+            e[j + 1].record()
+    torch.cuda.synchronize()
+    ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(calls))]
+    row_bytes = K.shape[1] * K.shape[2] * 2
+    cat_bytes = 2 * 2 * (n + nf) * row_bytes
+    return {"n_act": n, "n_frozen": nf, "schedule_frozen_ms": round(ms[0], 5), "concat_ms": round(ms[1], 5),
+            "concat_GB/s": round(cat_bytes / (ms[1] * 1e-3) / 1e9, 3), "attention_ms": round(ms[2], 4),
+            "path_ms": round(ms[1] + ms[2], 4)}
+
+
 def time_dense(torch, jano, Q, Kc, Vc, reps):
     out = torch.empty_like(Q)
     jano.attention(Q, Kc, Vc, out=out)
@@ -422,6 +459,12 @@ def main():
             if isinstance(v[kk], float):
                 v[kk] = round(v[kk], 5)
 
+    concat = None
+    if not args.no_extra:
+        print("bench: concatenated layout", file=sys.stderr, flush=True)
+        concat = time_concat_layout(torch, jano, p, Q, K, V)
+        concat["scatter_path_ms"] = round(per["scatter"] + per["attention"], 4)
+
     print("bench: write-back step", file=sys.stderr, flush=True)
     writeback = time_writeback(torch, jano, cfg, p.idx[:n_act])
 
@@ -482,6 +525,8 @@ def main():
         "kernels": kernels,
         "writeback": writeback,
     }
+    if concat is not None:
+        line["concat_layout"] = concat
     line.update(extra)
     print(json.dumps(line), flush=True)
 

@@ -143,6 +143,16 @@ int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *s
                   int step, int32_t *idx, int32_t *n_act_dev, void *stream);
 
 /*
+ * jano_schedule_frozen -- the complement of jano_schedule: ascending indices
+ * of the tokens NOT computed at `step` (their keys/values come from the cache),
+ * as used by the concatenated layout. Arguments as jano_schedule; empty at
+ * warm-up and cool-down steps.
+ * Pages: nl methodology §2; zh §2.2 item 3 (frozen tokens' cached K/V).
+ */
+int jano_schedule_frozen(const uint8_t *levels, const jano_grid *g, const jano_sched *sc,
+                         int step, int32_t *idx, int32_t *n_frozen_dev, void *stream);
+
+/*
  * jano_gather_rows -- adaptive token activation: X_act[i,:] = X[idx[i],:].
  * Pages: nl contributions item 2 (adaptive token activation); zh §3 item 2.
  *   X [N][D] bf16, idx [n_act] int32 in [0, N), X_act (out) [n_act][D] bf16.
@@ -161,6 +171,22 @@ int jano_gather_rows(const uint16_t *X, int64_t N, int64_t D, const int32_t *idx
 int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t *idx,
                     int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int64_t HD,
                     void *stream);
+
+/*
+ * jano_concat_kv -- the pages' layout of an interleaved step: fresh K/V rows of
+ * the active tokens first, then the cached rows of the frozen tokens, with
+ * positions not restored (attention does not depend on key order).
+ * Pages: nl methodology §2; fr §2.B; ko KV-cache item.
+ *   K_new, V_new [n_act][HD] bf16 (fresh rows); Kc, Vc [N][HD] bf16 cache;
+ *   frozen_idx [n_frozen] indices into the cache (from jano_schedule_frozen);
+ *   Kcat, Vcat (out) [n_act + n_frozen][HD]:
+ *     Kcat[r] = K_new[r] for r < n_act, Kc[frozen_idx[r - n_act]] after.
+ * The scatter cache (jano_attn_step) gives the same attention output with
+ * fewer bytes moved; this call exists to measure and test the pages' variant.
+ */
+int jano_concat_kv(const uint16_t *K_new, const uint16_t *V_new, int64_t n_act,
+                   const uint16_t *Kc, const uint16_t *Vc, const int32_t *frozen_idx,
+                   int64_t n_frozen, uint16_t *Kcat, uint16_t *Vcat, int64_t HD, void *stream);
 
 /*
  * jano_attention -- non-causal softmax attention of n_q queries against all

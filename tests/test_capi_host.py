@@ -153,6 +153,15 @@ def test_rows_and_attention_argument_errors():
     assert L.jano_attn_step(f, f, f, f, 4, f, f, 10, 2, 80, 0.0, f, None) == -2
     assert L.jano_attn_step(f, n, f, f, 4, f, f, 10, 2, 64, 0.0, f, None) == -1
     assert L.jano_check_idx(f, 4, 10, n, None) == -1
+    # concatenated layout: negative counts, null outputs, null sources
+    cc = L.jano_concat_kv
+    assert cc(f, f, -1, f, f, f, 3, f, f, 8, None) == -1
+    assert cc(f, f, 2, f, f, f, 3, n, f, 8, None) == -1
+    assert cc(n, f, 2, f, f, f, 3, f, f, 8, None) == -1
+    assert cc(f, f, 2, n, f, f, 3, f, f, 8, None) == -1
+    assert cc(f, f, 2, f, f, n, 3, f, f, 8, None) == -1
+    assert cc(f, f, 2, f, f, f, 3, f, f, 0, None) == -1
+    assert cc(n, n, 0, n, n, n, 0, n, n, 8, None) == 0           # empty is a no-op
     # write-back: n_act > N, null state, non-finite dt, null rows with n_act > 0
     wb = L.jano_writeback_step
     assert wb(f, f, 11, f, f, 10, 4, ctypes.c_float(0.1), None) == -1

@@ -292,6 +292,13 @@ def test_schedule_all_steps_480p(torch):
         n = int(n.item())
         assert n == len(ref) == jano.schedule_count(counts, sc.T, sc.W, sc.Cd, sc.periods, s)
         np.testing.assert_array_equal(idx.cpu().numpy()[:n], ref)
+        # the complement list of the concatenated layout
+        fidx, nf = jano.schedule(lvd, spec, s, sc.T, sc.W, sc.Cd, sc.periods, frozen=True)
+        torch.cuda.synchronize()
+        fref = O.schedule_frozen(tl, s, sc.T, sc.W, sc.Cd, sc.periods)
+        nf = int(nf.item())
+        assert nf == len(fref) == cfg.N - n
+        np.testing.assert_array_equal(fidx.cpu().numpy()[:nf], fref)
 
 
 @pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V720], ids=lambda c: c.name)
@@ -434,3 +441,49 @@ def test_attention_closed_forms(torch):
     assert np.abs(out - mean[None]).max() <= 2e-2 * max(1.0, np.abs(mean).max())
     one = host_bf16_f64(jano.attention(dev_bf16(Qz), dev_bf16(K[:1]), dev_bf16(V[:1])))
     np.testing.assert_array_equal(one, np.broadcast_to(O.bf16_to_f64(V[:1]), one.shape))
+
+
+# ------------------------------------------------- concatenated K/V layout
+
+def _concat_case(torch, cfg, frac):
+    idx = _idx_for(cfg, frac)
+    lv = synth.active_level_map(cfg, frac)
+    tl = O.token_levels(lv, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    sc = cfg.schedule
+    frozen = O.schedule_frozen(tl, sc.W + 1, sc.T, sc.W, sc.Cd, sc.periods)
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    rng = np.random.default_rng(21)
+    Kst, Vst = Kb.copy(), Vb.copy()       # stale rows where the active tokens are
+    Kst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
+    Vst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
+    Kcat, Vcat = jano.concat_kv(dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev_bf16(Kst), dev_bf16(Vst),
+                                dev(frozen))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(Kcat), O.concat_kv(Kb[idx], Kst, frozen))
+    np.testing.assert_array_equal(host_bits(Vcat), O.concat_kv(Vb[idx], Vst, frozen))
+    return idx, Qb, Kb, Vb, Kst, Vst, Kcat, Vcat
+
+
+@pytest.mark.parametrize("cfg,frac", [(configs.TINY, 0.3), (configs.IMAGE, 0.3), (configs.V720, 0.25)],
+                         ids=["tiny-30", "image-30", "720p-25"])
+def test_concat_kv_bit_exact(torch, cfg, frac):
+    print("concat", cfg.name, frac, flush=True)
+    _concat_case(torch, cfg, frac)
+
+
+def test_concat_attention_equals_scatter_path(torch):
+    # the pages' layout and the scatter cache give the same attention output
+    # (to the kernel's rounding; key order differs), both within tolerance of
+    # the oracle
+    cfg = configs.IMAGE
+    idx, Qb, Kb, Vb, Kst, Vst, Kcat, Vcat = _concat_case(torch, cfg, 0.3)
+    Qd = dev_bf16(Qb[idx])
+    out_cat = jano.attention(Qd, Kcat, Vcat)
+    Kc, Vc = dev_bf16(Kst), dev_bf16(Vst)
+    out_sc = jano.attn_step(Qd, dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev(idx), Kc, Vc)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Qb[idx]), O.bf16_to_f64(O.concat_kv(Kb[idx], Kst, np.setdiff1d(
+        np.arange(cfg.N), idx))), O.bf16_to_f64(O.concat_kv(Vb[idx], Vst, np.setdiff1d(np.arange(cfg.N), idx))))
+    assert_attn_close(host_bf16_f64(out_cat), ref, "concat layout")
+    assert_attn_close(host_bf16_f64(out_sc), ref, "scatter layout")
+    assert_attn_close(host_bf16_f64(out_cat), host_bf16_f64(out_sc), "concat vs scatter")

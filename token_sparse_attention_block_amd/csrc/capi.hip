@@ -47,6 +47,29 @@ void due_flags(const jano_sched *sc, int step, int due[3]) {
   for (int i = 0; i < 3; ++i) due[i] = dense || ((step - sc->W) % sc->period[i] == 0);
 }
 
+int schedule_impl(const uint8_t *levels, const jano_grid *g, const jano_sched *sc, int step,
+                  int32_t *idx, int32_t *n_dev, bool frozen, hipStream_t stream) {
+  if (!levels || !idx || !n_dev) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a) || !sched_ok(sc) || step < 0 || step >= sc->T) return JANO_E_INVAL;
+  jano::SchedGeom s{};
+  s.Ft = g->F / g->pF;
+  s.Ht = g->H / g->pH;
+  s.Wt = g->W / g->pW;
+  const int64_t N = static_cast<int64_t>(s.Ft) * s.Ht * s.Wt;
+  if (N > kMaxRows) return JANO_E_UNSUPPORTED;
+  s.N = static_cast<int>(N);
+  s.pF = g->pF; s.pH = g->pH; s.pW = g->pW;
+  s.bF = g->bF; s.bH = g->bH; s.bW = g->bW;
+  s.nBF = a.nBF;
+  s.nBH = a.nBH;
+  s.nBW = a.nBW;
+  due_flags(sc, step, s.due);
+  if (frozen)
+    for (int i = 0; i < 3; ++i) s.due[i] = !s.due[i];
+  return hip_status(jano::launch_schedule(levels, s, idx, n_dev, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,25 +150,28 @@ int jano_analyze(const float *lat, const jano_grid *g, int static_permille, int 
   return hip_status(jano::launch_levels(scores, a, nS, nSM, levels, level_tok_counts, s));
 }
 
+int jano_schedule_frozen(const uint8_t *levels, const jano_grid *g, const jano_sched *sc, int step,
+                         int32_t *idx, int32_t *n_frozen_dev, void *stream) {
+  return schedule_impl(levels, g, sc, step, idx, n_frozen_dev, true, static_cast<hipStream_t>(stream));
+}
+
+int jano_concat_kv(const uint16_t *K_new, const uint16_t *V_new, int64_t n_act, const uint16_t *Kc,
+                   const uint16_t *Vc, const int32_t *frozen_idx, int64_t n_frozen, uint16_t *Kcat,
+                   uint16_t *Vcat, int64_t HD, void *stream) {
+  if (n_act < 0 || n_frozen < 0 || HD < 1 || n_act > kMaxRows || n_frozen > kMaxRows ||
+      n_act + n_frozen > kMaxRows)
+    return JANO_E_INVAL;
+  if (n_act + n_frozen == 0) return JANO_OK;
+  if (!Kcat || !Vcat) return JANO_E_INVAL;
+  if (n_act > 0 && (!K_new || !V_new)) return JANO_E_INVAL;
+  if (n_frozen > 0 && (!Kc || !Vc || !frozen_idx)) return JANO_E_INVAL;
+  return hip_status(jano::launch_concat_kv(K_new, V_new, n_act, Kc, Vc, frozen_idx, n_frozen, Kcat, Vcat,
+                                           HD, static_cast<hipStream_t>(stream)));
+}
+
 int jano_schedule(const uint8_t *levels, const jano_grid *g, const jano_sched *sc, int step,
                   int32_t *idx, int32_t *n_act_dev, void *stream) {
-  if (!levels || !idx || !n_act_dev) return JANO_E_INVAL;
-  AnalyzeGeom a;
-  if (!grid_ok(g, &a) || !sched_ok(sc) || step < 0 || step >= sc->T) return JANO_E_INVAL;
-  jano::SchedGeom s{};
-  s.Ft = g->F / g->pF;
-  s.Ht = g->H / g->pH;
-  s.Wt = g->W / g->pW;
-  const int64_t N = static_cast<int64_t>(s.Ft) * s.Ht * s.Wt;
-  if (N > kMaxRows) return JANO_E_UNSUPPORTED;
-  s.N = static_cast<int>(N);
-  s.pF = g->pF; s.pH = g->pH; s.pW = g->pW;
-  s.bF = g->bF; s.bH = g->bH; s.bW = g->bW;
-  s.nBF = a.nBF;
-  s.nBH = a.nBH;
-  s.nBW = a.nBW;
-  due_flags(sc, step, s.due);
-  return hip_status(jano::launch_schedule(levels, s, idx, n_act_dev, static_cast<hipStream_t>(stream)));
+  return schedule_impl(levels, g, sc, step, idx, n_act_dev, false, static_cast<hipStream_t>(stream));
 }
 
 int jano_gather_rows(const uint16_t *X, int64_t N, int64_t D, const int32_t *idx, int64_t n_act,

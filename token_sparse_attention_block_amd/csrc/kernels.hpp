@@ -57,6 +57,10 @@ hipError_t launch_scatter_kv(const uint16_t *Kn, const uint16_t *Vn, const int32
 // out_full-style single-tensor row scatter: dst[idx[i]] = src[i], rows of D bf16
 hipError_t launch_scatter_rows(const uint16_t *src, int64_t D, const int32_t *idx, int64_t n,
                                uint16_t *dst, hipStream_t s);
+// Kcat = [Kn rows 0..n_act) ; Kc[frozen[0..n_frozen))], same for V; rows of HD bf16
+hipError_t launch_concat_kv(const uint16_t *Kn, const uint16_t *Vn, int64_t n_act, const uint16_t *Kc,
+                            const uint16_t *Vc, const int32_t *frozen, int64_t n_frozen, uint16_t *Kcat,
+                            uint16_t *Vcat, int64_t HD, hipStream_t s);
 // x[e] = fma(dt, v[e], x[e]) over total elements (v bf16, x fp32)
 hipError_t launch_euler(const uint16_t *v, float *x, int64_t total, float dt, hipStream_t s);
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K,

@@ -92,6 +92,35 @@ __global__ __launch_bounds__(kMaxRowThreads) void scatter_rows_v16(const u32x4 *
     __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
 }
 
+// The pages' layout of one interleaved step ([nl] methodology §2, [fr] §2.B):
+// row r of Kcat/Vcat is the fresh row r of an active token for r < n_act and
+// the cached row frozen[r - n_act] of a frozen token after that; positions
+// are not restored. blockIdx.y selects K (0) or V (1).
+__global__ __launch_bounds__(kMaxRowThreads) void concat_kv_v16(
+    const u32x4 *__restrict__ kn, const u32x4 *__restrict__ vn, const u32x4 *__restrict__ kc,
+    const u32x4 *__restrict__ vc, const int32_t *__restrict__ frozen, long long n_act,
+    u32x4 *__restrict__ kcat, u32x4 *__restrict__ vcat, int chunks) {
+  const long long row = blockIdx.x;
+  const bool isk = blockIdx.y == 0;
+  const u32x4 *s = row < n_act ? (isk ? kn : vn) + row * chunks
+                               : (isk ? kc : vc) + static_cast<long long>(frozen[row - n_act]) * chunks;
+  u32x4 *d = (isk ? kcat : vcat) + row * chunks;
+  for (int c = threadIdx.x; c < chunks; c += blockDim.x)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+}
+
+__global__ __launch_bounds__(kRowThreads) void concat_kv_u16(
+    const uint16_t *__restrict__ kn, const uint16_t *__restrict__ vn, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ frozen, long long n_act,
+    uint16_t *__restrict__ kcat, uint16_t *__restrict__ vcat, long long D) {
+  const long long row = blockIdx.x;
+  const bool isk = blockIdx.y == 0;
+  const uint16_t *s = row < n_act ? (isk ? kn : vn) + row * D
+                                  : (isk ? kc : vc) + static_cast<long long>(frozen[row - n_act]) * D;
+  uint16_t *d = (isk ? kcat : vcat) + row * D;
+  for (long long c = threadIdx.x; c < D; c += kRowThreads) d[c] = s[c];
+}
+
 // rows of at most 32 chunks: several rows per workgroup, one thread per chunk
 constexpr int kSmallRowThreads = 256;
 __global__ __launch_bounds__(kSmallRowThreads) void scatter_rows_small_v16(const u32x4 *__restrict__ src,
@@ -208,6 +237,27 @@ hipError_t launch_scatter_rows(const uint16_t *src, int64_t D, const int32_t *id
   } else {
     hipLaunchKernelGGL(scatter_rows_u16, dim3(static_cast<unsigned>(n)), dim3(kRowThreads), 0, s, src,
                        idx, dst, static_cast<long long>(D));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_concat_kv(const uint16_t *Kn, const uint16_t *Vn, int64_t n_act, const uint16_t *Kc,
+                            const uint16_t *Vc, const int32_t *frozen, int64_t n_frozen, uint16_t *Kcat,
+                            uint16_t *Vcat, int64_t HD, hipStream_t s) {
+  const int64_t rows = n_act + n_frozen;
+  if (rows == 0) return hipSuccess;
+  const bool fresh_ok = n_act == 0 || (aligned16(Kn) && aligned16(Vn));
+  if ((HD * 2) % 16 == 0 && fresh_ok && aligned16(Kc) && aligned16(Vc) && aligned16(Kcat) &&
+      aligned16(Vcat)) {
+    const int chunks = static_cast<int>(HD * 2 / 16);
+    hipLaunchKernelGGL(concat_kv_v16, dim3(static_cast<unsigned>(rows), 2), dim3(row_threads(chunks)), 0, s,
+                       reinterpret_cast<const u32x4 *>(Kn), reinterpret_cast<const u32x4 *>(Vn),
+                       reinterpret_cast<const u32x4 *>(Kc), reinterpret_cast<const u32x4 *>(Vc), frozen,
+                       static_cast<long long>(n_act), reinterpret_cast<u32x4 *>(Kcat),
+                       reinterpret_cast<u32x4 *>(Vcat), chunks);
+  } else {
+    hipLaunchKernelGGL(concat_kv_u16, dim3(static_cast<unsigned>(rows), 2), dim3(kRowThreads), 0, s, Kn, Vn,
+                       Kc, Vc, frozen, static_cast<long long>(n_act), Kcat, Vcat, static_cast<long long>(HD));
   }
   return hipGetLastError();
 }

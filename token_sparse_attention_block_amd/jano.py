@@ -20,7 +20,8 @@ JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_
 EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
     "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_levels", "jano_analyze",
-    "jano_schedule", "jano_gather_rows", "jano_writeback_step",
+    "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
+    "jano_writeback_step",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
 )
 
@@ -79,6 +80,8 @@ def lib():
             "jano_grid_sizes": ([gp, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
             "jano_schedule_count": ([ctypes.POINTER(ctypes.c_int32), sp, i32, ctypes.POINTER(i64)], i32),
             "jano_analyze_workspace_bytes": ([gp], ctypes.c_size_t),
+            "jano_schedule_frozen": ([vp, gp, sp, i32, vp, vp, vp], i32),
+            "jano_concat_kv": ([vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp], i32),
             "jano_writeback_step": ([vp, vp, i64, vp, vp, i64, i64, ctypes.c_float, vp], i32),
             "jano_analyze_scores": ([vp, gp, vp, vp, ctypes.c_size_t, vp], i32),
             "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
@@ -224,8 +227,10 @@ def levels(scores, spec: GridSpec, static_permille=400, moderate_permille=300, l
     return lv, counts
 
 
-def schedule(levels, spec: GridSpec, step, T=50, W=5, Cd=5, periods=(4, 2, 1), idx=None, n_act=None):
-    """jano_schedule -> (idx int32 [N] (first n_act valid), n_act int32 [1]) on device."""
+def schedule(levels, spec: GridSpec, step, T=50, W=5, Cd=5, periods=(4, 2, 1), idx=None, n_act=None,
+             frozen=False):
+    """jano_schedule (frozen=False) or jano_schedule_frozen (frozen=True) ->
+    (idx int32 [N] (first n valid), n int32 [1]) on device."""
     torch = _torch()
     B, N = grid_sizes(spec)
     _need(levels, "levels", torch.uint8, (B,))
@@ -238,8 +243,9 @@ def schedule(levels, spec: GridSpec, step, T=50, W=5, Cd=5, periods=(4, 2, 1), i
     _need(n_act, "n_act", torch.int32, (1,), dev)
     g = spec.c()
     sc = Sched(T, W, Cd, (ctypes.c_int32 * 3)(*periods))
-    _check("jano_schedule", lib().jano_schedule(_ptr(levels), ctypes.byref(g), ctypes.byref(sc),
-                                                int(step), _ptr(idx), _ptr(n_act), _stream(levels)))
+    name = "jano_schedule_frozen" if frozen else "jano_schedule"
+    _check(name, getattr(lib(), name)(_ptr(levels), ctypes.byref(g), ctypes.byref(sc), int(step),
+                                      _ptr(idx), _ptr(n_act), _stream(levels)))
     return idx, n_act
 
 
@@ -330,6 +336,39 @@ def attn_step(Q_act, K_new, V_new, idx, Kc, Vc, scale=0.0, out=None, n_act=None)
         _ptr(Q_act), _ptr(K_new), _ptr(V_new), _ptr(idx), n, _ptr(Kc), _ptr(Vc), N, H, d,
         float(scale), _ptr(out), _stream(Kc)))
     return out
+
+
+def concat_kv(K_new, V_new, Kc, Vc, frozen_idx, n_act=None, n_frozen=None, Kcat=None, Vcat=None):
+    """jano_concat_kv: [fresh rows ; cached rows of the frozen tokens] for K
+    and V. K_new/V_new [>= n_act, H, d], Kc/Vc [N, H, d] bf16 on device ->
+    (Kcat, Vcat) [n_act + n_frozen, H, d]."""
+    torch = _torch()
+    _need(Kc, "Kc", torch.bfloat16)
+    if Kc.dim() != 3:
+        raise ValueError("Kc must be [N, H, d]")
+    N, H, d = Kc.shape
+    dev = Kc.device
+    _need(Vc, "Vc", torch.bfloat16, (N, H, d), dev)
+    na = K_new.shape[0] if n_act is None else int(n_act)
+    nf = frozen_idx.numel() if n_frozen is None else int(n_frozen)
+    for name, t in (("K_new", K_new), ("V_new", V_new)):
+        _need(t, name, torch.bfloat16, None, dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (H, d) or t.shape[0] < na:
+            raise ValueError("%s must be [>= n_act, %d, %d]" % (name, H, d))
+    _need(frozen_idx, "frozen_idx", torch.int32, None, dev)
+    if nf > frozen_idx.numel():
+        raise ValueError("n_frozen exceeds frozen_idx length")
+    rows = na + nf
+    Kcat = torch.empty((rows, H, d), dtype=torch.bfloat16, device=dev) if Kcat is None else Kcat
+    Vcat = torch.empty((rows, H, d), dtype=torch.bfloat16, device=dev) if Vcat is None else Vcat
+    for name, t in (("Kcat", Kcat), ("Vcat", Vcat)):
+        _need(t, name, torch.bfloat16, None, dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (H, d) or t.shape[0] < rows:
+            raise ValueError("%s must be [>= n_act + n_frozen, %d, %d]" % (name, H, d))
+    _check("jano_concat_kv", lib().jano_concat_kv(
+        _ptr(K_new), _ptr(V_new), na, _ptr(Kc), _ptr(Vc), _ptr(frozen_idx), nf, _ptr(Kcat),
+        _ptr(Vcat), H * d, _stream(Kc)))
+    return Kcat, Vcat
 
 
 def writeback_step(out_act, idx, out_full, x, dt, n_act=None):
