@@ -321,3 +321,61 @@ def writeback_step(out_act_bits, idx, out_full_bits, x, dt):
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     x2 = x64 + np.float64(np.float32(dt)) * bf16_to_f64(of)
     return of, x2.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Projection of the active tokens' hidden states to Q, K, V with a 3D rotary
+# position encoding. The pages place only the active tokens' computation in
+# the interleaved step ([nl] methodology §2; [zh] §2.2 item 3) and cache keys
+# without restoring positions ([fr] §2.B), so the cached keys already carry
+# their position encoding. The projection itself and the encoding are model
+# details the pages do not give; reading taken: y = W x with W [3*H*d, Dm]
+# (rows Q, then K, then V; head-major, then dim), and a rotary encoding of Q
+# and K over the token's (frame, row, column): the head dim splits into three
+# even parts d_f = d - 4*floor(d/6), d_h = d_w = 2*floor(d/6); pair i of a
+# part of size m rotates dims (2i, 2i+1) of that part by pos * base**(-2i/m).
+# --------------------------------------------------------------------------
+
+def rope_parts(d: int) -> tuple:
+    dh = 2 * (d // 6)
+    return d - 2 * dh, dh, dh
+
+
+def rope_apply(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """x [n, H, d] (float), pos [n, 3] integer (frame, row, column)."""
+    x = np.asarray(x, dtype=np.float64)
+    n, Hh, d = x.shape
+    out = np.empty_like(x)
+    j0 = 0
+    for axis, m in enumerate(rope_parts(d)):
+        for i in range(m // 2):
+            ang = pos[:, axis].astype(np.float64) * base ** (-2.0 * i / m)
+            c, s = np.cos(ang)[:, None], np.sin(ang)[:, None]
+            a, b = x[:, :, j0 + 2 * i], x[:, :, j0 + 2 * i + 1]
+            out[:, :, j0 + 2 * i] = a * c - b * s
+            out[:, :, j0 + 2 * i + 1] = a * s + b * c
+        j0 += m
+    return out
+
+
+def token_positions(idx: np.ndarray, token_grid) -> np.ndarray:
+    """(frame, row, column) of token-major indices n = (f * Ht + h) * Wt + w."""
+    Ft, Ht, Wt = token_grid
+    idx = np.asarray(idx, dtype=np.int64)
+    return np.stack([idx // (Ht * Wt), (idx // Wt) % Ht, idx % Wt], axis=1)
+
+
+def qkv_proj(X_bits, idx, W_bits, H: int, d: int, token_grid=None, base: float = 10000.0):
+    """Q, K, V [n_act, H, d] in fp64 for the active tokens idx.
+
+    X_bits [N, Dm] bf16 hidden states, W_bits [3*H*d, Dm] bf16 weights.
+    Y = X[idx] W^T exactly in fp64; Q and K are rotated when token_grid is
+    given (base > 0), V never."""
+    Xa = bf16_to_f64(np.asarray(X_bits)[np.asarray(idx, dtype=np.int64)])
+    Y = Xa @ bf16_to_f64(W_bits).T
+    n = Y.shape[0]
+    Q, K, V = (Y[:, p * H * d:(p + 1) * H * d].reshape(n, H, d) for p in range(3))
+    if token_grid is not None and base > 0:
+        pos = token_positions(idx, token_grid)
+        Q, K = rope_apply(Q, pos, base), rope_apply(K, pos, base)
+    return Q, K, V

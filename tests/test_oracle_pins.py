@@ -428,3 +428,85 @@ def test_concat_layout_rows():
         assert cat[i].tolist() == Kn[i].tolist()
     for j, r in enumerate(frozen):
         assert cat[2 + j].tolist() == Kc[r].tolist()
+
+
+# ------------------------------------------------------- projection + RoPE
+
+def test_rope_parts_and_identity_at_origin():
+    assert O.rope_parts(128) == (44, 42, 42) and O.rope_parts(64) == (24, 20, 20)
+    assert O.rope_parts(6) == (2, 2, 2)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 2, 128))
+    np.testing.assert_array_equal(O.rope_apply(x, np.zeros((3, 3), np.int64), 10000.0), x)
+
+
+def test_rope_closed_form_d6():
+    # d = 6: one pair per axis, frequency base**0 = 1, so the angle is the position
+    x = np.array([[[1.0, 0.0, 1.0, 0.0, 0.0, 2.0]]])
+    pos = np.array([[1, 2, 3]])
+    y = O.rope_apply(x, pos, 10000.0)[0, 0]
+    np.testing.assert_allclose(y[:2], [np.cos(1), np.sin(1)], atol=1e-15)
+    np.testing.assert_allclose(y[2:4], [np.cos(2), np.sin(2)], atol=1e-15)
+    np.testing.assert_allclose(y[4:], [-2 * np.sin(3), 2 * np.cos(3)], atol=1e-15)
+
+
+def test_rope_relative_position_property():
+    # <rope(q, p1), rope(k, p2)> depends only on p1 - p2, per axis, and pair
+    # norms are kept
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    def dot(p1, p2):
+        return float(np.sum(O.rope_apply(q, np.array([p1]), 500.0) * O.rope_apply(k, np.array([p2]), 500.0)))
+    assert abs(dot([3, 5, 7], [1, 2, 4]) - dot([12, 9, 10], [10, 6, 7])) < 1e-9
+    assert abs(dot([3, 5, 7], [1, 2, 4]) - dot([3, 5, 7], [1, 2, 5])) > 1e-6
+    r = O.rope_apply(q, np.array([[4, 1, 9]]), 10000.0)
+    np.testing.assert_allclose(r[0, 0, ::2] ** 2 + r[0, 0, 1::2] ** 2, q[0, 0, ::2] ** 2 + q[0, 0, 1::2] ** 2)
+
+
+def test_token_positions():
+    pos = O.token_positions(np.array([0, 1, 5, 6, 13]), (2, 2, 3))
+    assert pos.tolist() == [[0, 0, 0], [0, 0, 1], [0, 1, 2], [1, 0, 0], [2, 0, 1]]
+
+
+def test_qkv_proj_identity_weights_and_bruteforce():
+    rng = np.random.default_rng(5)
+    H, d, N = 2, 6, 7
+    X = synth.f32_to_bf16_bits(rng.standard_normal((N, H * d)).astype(np.float32))
+    eye = np.eye(H * d, dtype=np.float32)
+    W = synth.f32_to_bf16_bits(np.concatenate([eye, 2 * eye, -eye]))
+    idx = np.array([1, 4, 6])
+    Q, K, V = O.qkv_proj(X, idx, W, H, d)
+    xa = O.bf16_to_f64(X[idx]).reshape(3, H, d)
+    np.testing.assert_array_equal(Q, xa)
+    np.testing.assert_array_equal(K, 2 * xa)
+    np.testing.assert_array_equal(V, -xa)
+    # brute force with Python loops on random weights, with the rotation
+    W = synth.f32_to_bf16_bits(rng.standard_normal((3 * H * d, H * d)).astype(np.float32))
+    Q, K, V = O.qkv_proj(X, idx, W, H, d, token_grid=(1, 1, N), base=100.0)
+    Wf, Xf = O.bf16_to_f64(W), O.bf16_to_f64(X)
+    for a, n in enumerate(idx):
+        y = [sum(Wf[o, e] * Xf[n, e] for e in range(H * d)) for o in range(3 * H * d)]
+        v = np.array(y[2 * H * d:]).reshape(H, d)
+        np.testing.assert_allclose(V[a], v, rtol=1e-12, atol=1e-12)
+        q = np.array(y[:H * d]).reshape(1, H, d)
+        pos = np.array([[0, 0, n]])
+        np.testing.assert_allclose(Q[a], O.rope_apply(q, pos, 100.0)[0], rtol=1e-12, atol=1e-12)
+        # the column axis is the last part (dims 4, 5 for d = 6): angle n * 1
+        qq = q[0, :, 4:6]
+        want = np.stack([qq[:, 0] * np.cos(n) - qq[:, 1] * np.sin(n), qq[:, 0] * np.sin(n) + qq[:, 1] * np.cos(n)], 1)
+        np.testing.assert_allclose(Q[a][:, 4:6], want, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_second_pair_frequency():
+    # d = 12: parts of 4; pair 1 of a part turns by pos * base**(-2/4), which
+    # at base 100 and position 10 is exactly 1 radian (frame part, dims 2, 3)
+    x = np.zeros((1, 1, 12))
+    x[0, 0, 2] = 1.0
+    y = O.rope_apply(x, np.array([[10, 0, 0]]), 100.0)[0, 0]
+    np.testing.assert_allclose(y[2:4], [np.cos(1.0), np.sin(1.0)], atol=1e-14)
+    # the row part starts at dim 4: its pair 0 turns by the row position
+    x = np.zeros((1, 1, 12))
+    x[0, 0, 4] = 1.0
+    y = O.rope_apply(x, np.array([[10, 3, 0]]), 100.0)[0, 0]
+    np.testing.assert_allclose(y[4:6], [np.cos(3.0), np.sin(3.0)], atol=1e-14)
