@@ -294,6 +294,34 @@ def time_concat_layout(torch, jano, p, Q, K, V, reps=3):
             "path_ms": round(ms[1] + ms[2], 4)}
 
 
+def time_qkv_proj(torch, jano, cfg, idx, reps=5):
+    """jano_qkv_proj on the active tokens: hidden size H*d (5120 for 40 x 128),
+    random weights, rotary encoding on the token grid. Rows of the hidden
+    states that are not active are never read."""
+    H, d = cfg.heads, cfg.d
+    Dm, n = H * d, idx.numel()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    X = torch.randn((cfg.N, Dm), generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((3 * H * d, Dm), generator=g, device="cuda") / 64).to(torch.bfloat16)
+    spec = jano.GridSpec.of(cfg)
+    out = tuple(torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    for _ in range(2):
+        jano.qkv_proj(X, idx, W, H, d, spec, 10000.0, out=out)
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(reps):
+        jano.qkv_proj(X, idx, W, H, d, spec, 10000.0, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 2.0 * n * Dm * 3 * H * d
+    tf = flops / (ms * 1e-3) / 1e12
+    del X, W, out
+    return {"ms": round(ms, 4), "n_act": n, "hidden": Dm, "out_features": 3 * H * d,
+            "flops": flops, "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 5)}
+
+
 def time_dense(torch, jano, Q, Kc, Vc, reps):
     out = torch.empty_like(Q)
     jano.attention(Q, Kc, Vc, out=out)
@@ -465,6 +493,11 @@ def main():
         concat = time_concat_layout(torch, jano, p, Q, K, V)
         concat["scatter_path_ms"] = round(per["scatter"] + per["attention"], 4)
 
+    proj = None
+    if not args.no_extra:
+        print("bench: QKV projection", file=sys.stderr, flush=True)
+        proj = time_qkv_proj(torch, jano, cfg, p.idx[:n_act])
+
     print("bench: write-back step", file=sys.stderr, flush=True)
     writeback = time_writeback(torch, jano, cfg, p.idx[:n_act])
 
@@ -527,6 +560,8 @@ def main():
     }
     if concat is not None:
         line["concat_layout"] = concat
+    if proj is not None:
+        line["qkv_proj"] = proj
     line.update(extra)
     print(json.dumps(line), flush=True)
 

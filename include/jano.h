@@ -189,6 +189,29 @@ int jano_concat_kv(const uint16_t *K_new, const uint16_t *V_new, int64_t n_act,
                    int64_t n_frozen, uint16_t *Kcat, uint16_t *Vcat, int64_t HD, void *stream);
 
 /*
+ * jano_qkv_proj -- project the active tokens' hidden states to Q, K, V and
+ * apply a 3D rotary position encoding to Q and K.
+ * Pages: only the active tokens are computed in an interleaved step (nl
+ * methodology §2; zh §2.2 item 3) and cached keys keep the encoding they were
+ * computed with, positions never restored (fr §2.B). The projection and the
+ * encoding are model details the pages do not give; the form here:
+ *   y = W x[idx[i]]                 W = Wqkv [3*H*d][Dm] bf16 (rows Q, K, V;
+ *                                   head-major then dim), x = X [N][Dm] bf16,
+ *                                   fp32 accumulation;
+ *   Q, K rotated per token position (frame, row, column) of token idx[i] in
+ *   the token grid of g: the head dim splits into d_f = d - 4*floor(d/6) and
+ *   d_h = d_w = 2*floor(d/6) dims; pair k of a part of m dims turns dims
+ *   (2k, 2k+1) of that part by pos * rope_base^(-2k/m).
+ *   g NULL or rope_base <= 0: no rotation (g may then be NULL).
+ *   Q, K_new, V_new (out) [n_act][H][d] bf16, 16-byte aligned.
+ * Needs Dm a multiple of 32, d a multiple of 4 (and >= 6 with rotation),
+ * N*Dm*2 < 2^32 bytes (JANO_E_UNSUPPORTED otherwise); idx entries in [0, N).
+ */
+int jano_qkv_proj(const uint16_t *X, int64_t N, int64_t Dm, const int32_t *idx, int64_t n_act,
+                  const uint16_t *Wqkv, int H, int d, const jano_grid *g, float rope_base,
+                  uint16_t *Q, uint16_t *K_new, uint16_t *V_new, void *stream);
+
+/*
  * jano_attention -- non-causal softmax attention of n_q queries against all
  * N cached keys/values, per head: out[i,h] = softmax(Q[i,h] Kc[:,h]^T * scale) Vc[:,h].
  * Pages: full attention over all tokens, quadratic in sequence length

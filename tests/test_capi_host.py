@@ -153,6 +153,18 @@ def test_rows_and_attention_argument_errors():
     assert L.jano_attn_step(f, f, f, f, 4, f, f, 10, 2, 80, 0.0, f, None) == -2
     assert L.jano_attn_step(f, n, f, f, 4, f, f, 10, 2, 64, 0.0, f, None) == -1
     assert L.jano_check_idx(f, 4, 10, n, None) == -1
+    # projection: unsupported Dm / d, bad token grid for the rotation, nulls
+    qp = L.jano_qkv_proj
+    g = _grid()    # token grid 3 x 16 x 16 = 768 tokens
+    c = ctypes.c_float
+    assert qp(f, 768, 100, f, 4, f, 2, 64, None, c(0.0), f, f, f, None) == -2     # Dm % 32
+    assert qp(f, 768, 128, f, 4, f, 2, 62, None, c(0.0), f, f, f, None) == -2     # d % 4
+    assert qp(f, 767, 128, f, 4, f, 2, 64, ctypes.byref(g), c(1e4), f, f, f, None) == -1  # N != grid
+    assert qp(f, 768, 128, f, 4, f, 2, 4, ctypes.byref(g), c(1e4), f, f, f, None) == -1   # d < 6 rotated
+    assert qp(f, 768, 128, f, 4, f, 2, 64, None, c(float("nan")), f, f, f, None) == -1
+    assert qp(f, 768, 128, n, 4, f, 2, 64, None, c(0.0), f, f, f, None) == -1
+    assert qp(f, 768, 128, f, 4, f, 2, 64, None, c(0.0), f, n, f, None) == -1
+    assert qp(n, 768, 128, n, 0, n, 2, 64, None, c(0.0), n, n, n, None) == 0       # nothing active
     # concatenated layout: negative counts, null outputs, null sources
     cc = L.jano_concat_kv
     assert cc(f, f, -1, f, f, f, 3, f, f, 8, None) == -1

@@ -487,3 +487,58 @@ def test_concat_attention_equals_scatter_path(torch):
     assert_attn_close(host_bf16_f64(out_cat), ref, "concat layout")
     assert_attn_close(host_bf16_f64(out_sc), ref, "scatter layout")
     assert_attn_close(host_bf16_f64(out_cat), host_bf16_f64(out_sc), "concat vs scatter")
+
+
+# ------------------------------------------------ gathered QKV projection
+
+def _proj_close(got, ref, label):
+    got = np.asarray(got, np.float64)
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.max(np.abs(ref))
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (label, int(bad.sum()), float(np.abs(got - ref)[bad].max()))
+
+
+def _proj_run(torch, X_bits, idx, W_bits, H, d, spec, base):
+    Xd = dev_bf16(X_bits)
+    Q, K, V = jano.qkv_proj(Xd, dev(idx), dev_bf16(W_bits), H, d, spec, base)
+    torch.cuda.synchronize()
+    return [host_bf16_f64(t) for t in (Q, K, V)]
+
+
+@pytest.mark.parametrize("rotate", [False, True], ids=["plain", "rotary"])
+def test_qkv_proj_small_ragged(torch, rotate):
+    # 77 tokens (ragged token tile), 3*H*d = 384 columns (ragged column tile),
+    # Dm = 96 (three k tiles)
+    rng = np.random.default_rng(3)
+    spec = jano.GridSpec(3, 1, 3, 10, 10, (1, 5, 5), (1, 1, 1))     # token grid 3 x 10 x 10
+    N, Dm, H, d = 300, 96, 2, 64
+    X = synth.f32_to_bf16_bits(rng.standard_normal((N, Dm)).astype(np.float32))
+    W = synth.f32_to_bf16_bits((rng.standard_normal((3 * H * d, Dm)) / 8).astype(np.float32))
+    idx = np.sort(rng.choice(N, 77, replace=False)).astype(np.int32)
+    got = _proj_run(torch, X, idx, W, H, d, spec if rotate else None, 500.0)
+    ref = O.qkv_proj(X, idx, W, H, d, (3, 10, 10) if rotate else None, 500.0)
+    for name, g_, r_ in zip("QKV", got, ref):
+        _proj_close(g_, r_, name)
+
+
+def test_qkv_proj_full_size_sampled(torch):
+    # 720p token grid, hidden size 5120 = 40 heads x 128, 25% active; rows of
+    # X that are not active are never read, so only the active rows are set
+    cfg = configs.V720
+    spec = jano.GridSpec.of(cfg)
+    H, d, Dm = cfg.heads, cfg.d, cfg.heads * cfg.d
+    idx = _idx_for(cfg, 0.25)
+    rng = np.random.default_rng(5)
+    Xa = synth.f32_to_bf16_bits(rng.standard_normal((len(idx), Dm)).astype(np.float32))
+    W = synth.f32_to_bf16_bits((rng.standard_normal((3 * H * d, Dm)) / 64).astype(np.float32))
+    Xd = torch.zeros((cfg.N, Dm), dtype=torch.bfloat16, device="cuda")
+    Xd[torch.from_numpy(idx.astype(np.int64)).cuda()] = dev_bf16(Xa)
+    Q, K, V = jano.qkv_proj(Xd, dev(idx), dev_bf16(W), H, d, spec, 10000.0)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([rng.choice(len(idx), 200, replace=False), [0, len(idx) - 1]]))
+    Xs = np.zeros((cfg.N, Dm), np.uint16)
+    Xs[idx[sample]] = Xa[sample]
+    ref = O.qkv_proj(Xs, idx[sample], W, H, d, (cfg.F // cfg.patch[0], cfg.H // cfg.patch[1],
+                                                cfg.W // cfg.patch[2]), 10000.0)
+    for name, t, r_ in zip("QKV", (Q, K, V), ref):
+        _proj_close(host_bf16_f64(t)[sample], r_, name)

@@ -18,7 +18,7 @@ SRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libjano.so")
-SOURCES = ["capi.hip", "analyze.hip", "schedule.hip", "rows.hip", "attention.hip"]
+SOURCES = ["capi.hip", "analyze.hip", "schedule.hip", "rows.hip", "attention.hip", "proj.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

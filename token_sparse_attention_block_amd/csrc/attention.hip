@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_copy.hpp"
 
 namespace jano {
 namespace {
@@ -234,41 +235,13 @@ constexpr int kW2 = 8;                      // waves per workgroup
 constexpr int kRowB = 256;                  // bytes per K/V row (d = 128)
 constexpr int kTileB = kBN * kRowB;         // 16 KB per K or V tile
 constexpr float kRescaleSlack = 8.0f;       // log2 headroom before rescaling
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
-// vmcnt high bits [15:14]); expcnt and lgkmcnt at their "no wait" maximum.
-constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kWaitVmcnt4 = 0x0F74;
+constexpr int kWaitVmcnt0 = vmcnt_wait(0);
+constexpr int kWaitVmcnt4 = vmcnt_wait(4);
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ int swz_k(int r) { return r & 15; }
 
-// One global -> LDS copy of 16 bytes per lane: lane i's bytes land at
-// lds_base + 16*i. Issued from asm so that the compiler does not treat every
-// later LDS read as dependent on it (it would wait for all copies in flight,
-// including the tiles being prefetched); the kernel waits on vmcnt itself.
-// The instruction has no register results, only address operands.
-__device__ __forceinline__ void copy16_to_lds(const void *gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(gptr)
-               : "memory", "m0");
-}
-
-// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
-// byte offset (saddr form): advancing the base costs no vector instructions.
-__device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  const uint32_t a = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
-  return __builtin_amdgcn_readfirstlane(a);
-}
 
 
 constexpr int kStages = 4;

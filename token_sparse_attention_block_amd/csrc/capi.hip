@@ -226,6 +226,32 @@ int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t 
   return hip_status(jano::launch_attention(Q_act, n_act, Kc, Vc, N, H, d, sc, out, s));
 }
 
+int jano_qkv_proj(const uint16_t *X, int64_t N, int64_t Dm, const int32_t *idx, int64_t n_act,
+                  const uint16_t *Wqkv, int H, int d, const jano_grid *g, float rope_base,
+                  uint16_t *Q, uint16_t *K_new, uint16_t *V_new, void *stream) {
+  if (N < 1 || Dm < 1 || H < 1 || d < 1 || n_act < 0 || n_act > kMaxRows || N > kMaxRows ||
+      !isfinite(rope_base))
+    return JANO_E_INVAL;
+  if (!jano::qkv_proj_supported(N, Dm, H, d)) return JANO_E_UNSUPPORTED;
+  int Ht = 1, Wt = 1;
+  float base = 0.0f;
+  if (g && rope_base > 0.0f) {
+    AnalyzeGeom a;
+    if (!grid_ok(g, &a) || d < 6 || d % 2) return JANO_E_INVAL;
+    const int64_t Ft = g->F / g->pF;
+    Ht = g->H / g->pH;
+    Wt = g->W / g->pW;
+    if (Ft * Ht * Wt != N) return JANO_E_INVAL;
+    base = rope_base;
+  }
+  if (n_act == 0) return JANO_OK;
+  if (!X || !idx || !Wqkv || !Q || !K_new || !V_new) return JANO_E_INVAL;
+  if (!aligned16(X) || !aligned16(Wqkv) || !aligned16(Q) || !aligned16(K_new) || !aligned16(V_new))
+    return JANO_E_INVAL;
+  return hip_status(jano::launch_qkv_proj(X, Dm, idx, n_act, Wqkv, H, d, Ht, Wt, base, Q, K_new, V_new,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int jano_writeback_step(const uint16_t *out_act, const int32_t *idx, int64_t n_act,
                         uint16_t *out_full, float *x, int64_t N, int64_t P, float dt, void *stream) {
   if (N < 1 || P < 1 || n_act < 0 || n_act > N || N > kMaxRows || !isfinite(dt)) return JANO_E_INVAL;

@@ -63,6 +63,11 @@ hipError_t launch_concat_kv(const uint16_t *Kn, const uint16_t *Vn, int64_t n_ac
                             uint16_t *Vcat, int64_t HD, hipStream_t s);
 // x[e] = fma(dt, v[e], x[e]) over total elements (v bf16, x fp32)
 hipError_t launch_euler(const uint16_t *v, float *x, int64_t total, float dt, hipStream_t s);
+// gathered QKV projection (+ 3D rotary on Q, K); see proj.hip
+bool qkv_proj_supported(int64_t N, int64_t Dm, int H, int d);
+hipError_t launch_qkv_proj(const uint16_t *X, int64_t Dm, const int32_t *idx, int64_t n_act,
+                           const uint16_t *W, int H, int d, int Ht, int Wt, float rope_base,
+                           uint16_t *Q, uint16_t *Kn, uint16_t *Vn, hipStream_t s);
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K,
                             const uint16_t *V, int64_t N, int H, int d, float scale,
                             uint16_t *out, hipStream_t s);

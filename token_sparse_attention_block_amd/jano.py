@@ -21,7 +21,7 @@ EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
     "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_levels", "jano_analyze",
     "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
-    "jano_writeback_step",
+    "jano_writeback_step", "jano_qkv_proj",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
 )
 
@@ -82,6 +82,7 @@ def lib():
             "jano_analyze_workspace_bytes": ([gp], ctypes.c_size_t),
             "jano_schedule_frozen": ([vp, gp, sp, i32, vp, vp, vp], i32),
             "jano_concat_kv": ([vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp], i32),
+            "jano_qkv_proj": ([vp, i64, i64, vp, i64, vp, i32, i32, gp, ctypes.c_float, vp, vp, vp, vp], i32),
             "jano_writeback_step": ([vp, vp, i64, vp, vp, i64, i64, ctypes.c_float, vp], i32),
             "jano_analyze_scores": ([vp, gp, vp, vp, ctypes.c_size_t, vp], i32),
             "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
@@ -369,6 +370,35 @@ def concat_kv(K_new, V_new, Kc, Vc, frozen_idx, n_act=None, n_frozen=None, Kcat=
         _ptr(K_new), _ptr(V_new), na, _ptr(Kc), _ptr(Vc), _ptr(frozen_idx), nf, _ptr(Kcat),
         _ptr(Vcat), H * d, _stream(Kc)))
     return Kcat, Vcat
+
+
+def qkv_proj(X, idx, Wqkv, H, d, spec: GridSpec = None, rope_base=10000.0, n_act=None, out=None):
+    """jano_qkv_proj: X bf16 [N, Dm], idx int32, Wqkv bf16 [3*H*d, Dm] on
+    device -> (Q, K_new, V_new) bf16 [n_act, H, d]; rotary encoding on Q and
+    K when spec is given and rope_base > 0."""
+    torch = _torch()
+    _need(X, "X", torch.bfloat16)
+    if X.dim() != 2:
+        raise ValueError("X must be [N, Dm]")
+    N, Dm = X.shape
+    dev = X.device
+    _need(Wqkv, "Wqkv", torch.bfloat16, (3 * H * d, Dm), dev)
+    _need(idx, "idx", torch.int32, None, dev)
+    n = idx.numel() if n_act is None else int(n_act)
+    if n > idx.numel():
+        raise ValueError("n_act exceeds idx length")
+    if out is None:
+        out = tuple(torch.empty((n, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    for name, t in zip(("Q", "K_new", "V_new"), out):
+        _need(t, name, torch.bfloat16, None, dev)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (H, d) or t.shape[0] < n:
+            raise ValueError("%s must be [>= n_act, %d, %d]" % (name, H, d))
+    gp_ = ctypes.byref(spec.c()) if spec is not None else None
+    _check("jano_qkv_proj", lib().jano_qkv_proj(
+        _ptr(X), N, Dm, _ptr(idx), n, _ptr(Wqkv), int(H), int(d), gp_,
+        float(rope_base if spec is not None else 0.0), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+        _stream(X)))
+    return out
 
 
 def writeback_step(out_act, idx, out_full, x, dt, n_act=None):
