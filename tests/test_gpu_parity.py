@@ -505,13 +505,14 @@ def _proj_run(torch, X_bits, idx, W_bits, H, d, spec, base):
     return [host_bf16_f64(t) for t in (Q, K, V)]
 
 
-@pytest.mark.parametrize("rotate", [False, True], ids=["plain", "rotary"])
-def test_qkv_proj_small_ragged(torch, rotate):
+@pytest.mark.parametrize("rotate,Dm", [(False, 96), (True, 96), (True, 32), (False, 64), (True, 160)],
+                         ids=["plain-k3", "rotary-k3", "rotary-k1", "plain-k2", "rotary-k5"])
+def test_qkv_proj_small_ragged(torch, rotate, Dm):
     # 77 tokens (ragged token tile), 3*H*d = 384 columns (ragged column tile),
-    # Dm = 96 (three k tiles)
-    rng = np.random.default_rng(3)
+    # Dm / 32 k tiles (1, 2, 3 and 5 exercise the pipeline's start and tail)
+    rng = np.random.default_rng(3 + Dm)
     spec = jano.GridSpec(3, 1, 3, 10, 10, (1, 5, 5), (1, 1, 1))     # token grid 3 x 10 x 10
-    N, Dm, H, d = 300, 96, 2, 64
+    N, H, d = 300, 2, 64
     X = synth.f32_to_bf16_bits(rng.standard_normal((N, Dm)).astype(np.float32))
     W = synth.f32_to_bf16_bits((rng.standard_normal((3 * H * d, Dm)) / 8).astype(np.float32))
     idx = np.sort(rng.choice(N, 77, replace=False)).astype(np.int32)

@@ -16,15 +16,19 @@
 // tokens on N), so in the accumulator a lane holds four consecutive output
 // columns of one token: the rotary pairs are lane-local and each lane stores
 // 8 bytes per 16 x 16 tile. Workgroup tile 256 columns x 256 tokens, 8 waves
-// of 128 x 64; K advances 32 at a time through 4 LDS stages (two tiles in
-// flight) filled with global_load_lds_dwordx4. Token rows are gathered through
-// per-lane 32-bit offsets (idx[m] * Dm * 2) from a uniform base, weight rows
-// through fixed per-lane offsets, so no vector address arithmetic runs per
-// K step. LDS rows are 64 bytes (4 chunks); chunk c of row r sits in slot
-// c ^ ((r >> 2) & 3), which spreads the 16 rows one fragment read touches over
-// 16 bank groups. Workgroups are renumbered per XCD and rastered in groups of
-// 16 token tiles, so the workgroups that share token or weight tiles run on
-// one XCD (one L2) at the same time.
+// of 128 x 64. K advances 32 at a time through 4 LDS stages filled with
+// global_load_lds_dwordx4, three tiles in flight; a wave's MFMAs on tile t run
+// from registers while tile t+1 is published (barrier) and its fragments are
+// read, so LDS latency and the barrier overlap the MFMA work. Token rows are
+// gathered through per-lane 32-bit offsets (idx[m] * Dm * 2) from a uniform
+// base, weight rows through fixed per-lane offsets: no vector address
+// arithmetic per K step. LDS rows are 64 bytes (4 chunks); chunk c of row r
+// sits in slot c ^ ((r >> 1) & 3), so the 8 rows one 128-byte LDS pass of a
+// fragment read touches fall on 8 different 16-byte bank groups. Workgroups
+// are renumbered per XCD and rastered in groups of 2 token tiles (all weight
+// tiles of a group, token tile fastest), which keeps the weight tiles the
+// concurrent workgroups of an XCD share hot in its L2 (measured against groups
+// of 1, 3, 4, 6, 8, 16 and a weight-major raster).
 #include <math.h>
 
 #include "common.hpp"
@@ -42,11 +46,11 @@ constexpr int kPStages = 4;
 constexpr int kPRowB = kPBK * 2;          // 64 bytes per LDS row
 constexpr int kPTileB = kPBM * kPRowB;    // 16 KB per operand per stage
 constexpr int kPXcds = 8;
-constexpr int kPGroupM = 16;              // token tiles per raster group
+constexpr int kPGroupM = 2;              // token tiles per raster group
 
 typedef float f32x4p __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz_p(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_p(int r) { return (r >> 1) & 3; }
 
 struct ProjGeom {
   int n_act, Dm, Nout, HD, d;
@@ -106,9 +110,10 @@ __global__ __launch_bounds__(kPW * kWave) void qkv_proj_kernel(
   const int nk = g.Dm / kPBK;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
+  if (nk > 2) issue(2, 2);
 
   const int wn = wave % 2, wm = wave / 2;                        // wave tile: 128 columns x 64 tokens
-  const int frag = l16 * kPRowB + 16 * (h4 ^ ((l16 >> 2) & 3));  // row l16 of a 16-row block, k 8*h4..
+  const int frag = l16 * kPRowB + 16 * (h4 ^ ((l16 >> 1) & 3));  // row l16 of a 16-row block, k 8*h4..
   f32x4p acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
@@ -117,30 +122,56 @@ __global__ __launch_bounds__(kPW * kWave) void qkv_proj_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0f;
 
-  for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(4));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-    __builtin_amdgcn_s_barrier();
-    if (t + 2 < nk) issue(t + 2, (t + 2) % kPStages);
-    const char *ws = lds[t % kPStages][0];
-    const char *xs = lds[t % kPStages][1];
-    bf16x8 a[8], b[4];
+  bf16x8 fa0[8], fb0[4], fa1[8], fb1[4];
+  auto load_frags = [&](const int st, bf16x8 (&fa)[8], bf16x8 (&fb)[4]) __attribute__((always_inline)) {
+    const char *ws = lds[st][0];
+    const char *xs = lds[st][1];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
-      a[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                             ws + (128 * wn + 16 * nt) * kPRowB + frag));
+      fa[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                              ws + (128 * wn + 16 * nt) * kPRowB + frag));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-      b[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                             xs + (64 * wm + 16 * mt) * kPRowB + frag));
+      fb[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                              xs + (64 * wm + 16 * mt) * kPRowB + frag));
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[8], const bf16x8 (&fb)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nt], b[mt], acc[nt][mt], 0, 0, 0);
+        acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[nt], fb[mt], acc[nt][mt], 0, 0, 0);
+  };
+  // publish tile t (its copies and every wave's), then queue tile t + 2
+  // (every wave finished reading tile t-1 before this barrier, so tile t+3
+  // can take its stage: three tiles in flight)
+  auto publish = [&](const int t) __attribute__((always_inline)) {
+    if (t + 2 < nk)
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(8));
+    else if (t + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(4));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 3 < nk) issue(t + 3, (t + 3) % kPStages);
+  };
+  // tile t's MFMAs run from registers while tile t+1 is published and its
+  // fragments are read
+  publish(0);
+  load_frags(0, fa0, fb0);
+  int t = 0;
+  for (; t + 2 <= nk; t += 2) {
+    mfmas(fa0, fb0);
+    publish(t + 1);
+    load_frags((t + 1) % kPStages, fa1, fb1);
+    mfmas(fa1, fb1);
+    if (t + 2 < nk) {
+      publish(t + 2);
+      load_frags((t + 2) % kPStages, fa0, fb0);
+    }
   }
+  if (t < nk) mfmas(fa0, fb0);
 
   // epilogue: lane holds columns n .. n+3 of token m for every (nt, mt)
 #pragma unroll
