@@ -212,6 +212,25 @@ def test_levels_ties_and_max_size(torch, B_side, nvals):
             cnt.cpu().numpy(), O.level_token_counts(lv_ref, (spec.F, spec.H, spec.W), spec.patch, spec.block))
 
 
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.V720], ids=lambda c: c.name)
+def test_random_masking_index_source(torch, cfg):
+    # the pages' random-masking ablation as an index source: seeded random
+    # block scores through jano_levels and jano_schedule, bit-exact
+    spec = jano.GridSpec.of(cfg)
+    sc = synth.random_block_scores(cfg)
+    lv, cnt = jano.levels(dev(sc), spec, cfg.static_permille, cfg.moderate_permille)
+    lv_ref = O.assign_levels(sc, cfg.static_permille, cfg.moderate_permille)
+    np.testing.assert_array_equal(lv.cpu().numpy(), lv_ref)
+    tl = O.token_levels(lv_ref, (cfg.F, cfg.H, cfg.W), cfg.patch, cfg.block)
+    s_ = cfg.schedule
+    for step in (s_.W, s_.W + 1, s_.W + 2):
+        idx, n = jano.schedule(lv, spec, step, s_.T, s_.W, s_.Cd, s_.periods)
+        torch.cuda.synchronize()
+        ref = O.schedule(tl, step, s_.T, s_.W, s_.Cd, s_.periods)
+        assert int(n.item()) == len(ref)
+        np.testing.assert_array_equal(idx.cpu().numpy()[:len(ref)], ref)
+
+
 def test_analyze_scores_entry_point(torch):
     # the scores-only call equals jano_analyze's scores, bit for bit, every call
     cfg = configs.V480

@@ -510,3 +510,20 @@ def test_rope_second_pair_frequency():
     x[0, 0, 4] = 1.0
     y = O.rope_apply(x, np.array([[10, 3, 0]]), 100.0)[0, 0]
     np.testing.assert_allclose(y[4:6], [np.cos(3.0), np.sin(3.0)], atol=1e-14)
+
+
+# ------------------------------------------------- random-masking index source
+
+def test_random_masking_levels_have_exact_shares():
+    # ranking blocks by seeded random draws keeps the level shares exact and
+    # makes the split independent of the latents (the pages' ablation)
+    for cfg in (configs.TINY, configs.V480):
+        sc = synth.random_block_scores(cfg)
+        assert sc.dtype == np.float32 and np.all((sc >= 0) & (sc < 1))
+        lv = O.assign_levels(sc, cfg.static_permille, cfg.moderate_permille)
+        nS, nSM = O.level_split(cfg.B, cfg.static_permille, cfg.moderate_permille)
+        assert (lv == 1).sum() == nS and (lv == 2).sum() == nSM - nS and (lv == 3).sum() == cfg.B - nSM
+        order = np.argsort(sc, kind="stable")
+        assert np.all(lv[order[:nS]] == 1) and np.all(lv[order[nSM:]] == 3)
+        other = synth.random_block_scores(cfg, extra=1)
+        assert not np.array_equal(O.assign_levels(other, cfg.static_permille, cfg.moderate_permille), lv)

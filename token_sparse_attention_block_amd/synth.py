@@ -7,7 +7,8 @@ sharing any computation.
 
 Seeds are 20260000 + 100*cfg_id + role, with roles
   1 x0 background, 2 eps, 3 texture mask, 4/5/6 Q/K/V, 7 active-block mask,
-  8 moving-texture field, 9/10/11 Q/K/V drift directions (schedule run).
+  8 moving-texture field, 9/10/11 Q/K/V drift directions (schedule run),
+  12 random block scores (random-masking index source).
 
 The pages evaluate on real Flux-1-dev / Wan2.1 generations; these inputs stand
 in for them with the same token grids, following the configuration recipe:
@@ -20,6 +21,7 @@ import numpy as np
 
 ROLE_X0, ROLE_EPS, ROLE_TEX, ROLE_Q, ROLE_K, ROLE_V = 1, 2, 3, 4, 5, 6
 ROLE_ACTIVE, ROLE_FIELD, ROLE_DQ, ROLE_DK, ROLE_DV = 7, 8, 9, 10, 11
+ROLE_RANDOM_SCORES = 12
 
 
 def rng(cfg_id: int, role: int, extra: int = 0) -> np.random.Generator:
@@ -129,6 +131,13 @@ def active_level_map(cfg, frac: float) -> np.ndarray:
     lv = np.ones(B, dtype=np.uint8)
     lv[perm[:n]] = 3
     return lv
+
+
+def random_block_scores(cfg, extra: int = 0) -> np.ndarray:
+    """fp32 [B] uniform draws in [0, 1): ranking blocks by them instead of by
+    the analyzer's complexity gives the random-masking index source (the
+    pages' ablation); the level bucketing and schedule stay the same."""
+    return rng(cfg.cfg_id, ROLE_RANDOM_SCORES, extra).random(cfg.B, dtype=np.float32)
 
 
 def drift_qkv_f32(cfg, seed_extra: int = 0):
