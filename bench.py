@@ -17,8 +17,9 @@ the CPU oracle timed on a bounded sample.
     python bench.py [--steps K] [--warmup W] [--frac 0.25] [--no-cpu]
 
 HBM traffic (`roofline.traffic`) comes from profiles/traffic.json, written by
-    python bench.py --ingest-counters FETCH.csv WRITE.csv
-from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over
+    python bench.py --ingest-counters FETCH WRITE
+from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; each output a
+CSV or rocprofv3's SQLite .db) over
 `bench.py --steps 2 --warmup 0 --no-cpu --no-extra --calibrate-copy`; it is
 used only while the kernel sources still hash to what was profiled.
 """
@@ -63,7 +64,7 @@ def _short_kernel_name(name):
     return name.split("(")[0].split("<")[0]
 
 
-def ingest_counters(fetch_csv, write_csv, workload):
+def ingest_counters(fetch_path, write_path, workload):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) -> HBM bytes per launch.
 
     Each counter is scaled by what it reads for the 1 GiB device copy that
@@ -75,18 +76,34 @@ def ingest_counters(fetch_csv, write_csv, workload):
     import csv
     import statistics
 
+    def rows(path):
+        # rocprofv3 writes either a CSV (--output-format csv) or its SQLite
+        # database (the default): the same four fields from either
+        if path.endswith(".db"):
+            import sqlite3
+            con = sqlite3.connect(path)
+            try:
+                yield from con.execute("select counter_name, kernel_name, grid_size, dispatch_id, value "
+                                       "from counters_collection")
+            finally:
+                con.close()
+        else:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    yield (r["Counter_Name"], r["Kernel_Name"], r["Grid_Size"], r["Dispatch_Id"],
+                           r["Counter_Value"])
+
     def per_group(path, counter):
         groups = {}
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                k = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))
-                groups.setdefault(k, {}).setdefault(r["Dispatch_Id"], 0.0)
-                groups[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for name, kernel, grid, dispatch, value in rows(path):
+            if name != counter:
+                continue
+            k = (_short_kernel_name(kernel), int(grid))
+            groups.setdefault(k, {}).setdefault(str(dispatch), 0.0)
+            groups[k][str(dispatch)] += float(value)
         return groups
 
-    fg, wg = per_group(fetch_csv, "FETCH_SIZE"), per_group(write_csv, "WRITE_SIZE")
+    fg, wg = per_group(fetch_path, "FETCH_SIZE"), per_group(write_path, "WRITE_SIZE")
     gib_kib = float(1 << 20)
     # the calibration copy is the largest copy dispatch (the cache clones are smaller)
     copy_f = max(max(v.values()) for (n, _), v in fg.items() if n == "__amd_rocclr_copyBuffer")
@@ -422,8 +439,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline fraction only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc outputs (CSV or .db) and exit")
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, "720p-active%d" % round(100 * args.frac))

@@ -429,6 +429,16 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
         for (int g = 0; g < G; ++g)
           s[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[g][t], s[g][b], 0, 0, 0);
       }
+    // schedule: 4 K reads ahead, then one read per 3 MFMAs, so each read has
+    // 12 MFMAs (~190 cycles) to land; left to itself the compiler waits on
+    // each read right after issuing it
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // 4 LDS reads
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // 3 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);   // last 12 MFMAs
 
     bf16x8 pb[G][kBN / 32];
 #pragma unroll
