@@ -141,8 +141,8 @@ def random_block_scores(cfg, extra: int = 0) -> np.ndarray:
 
 
 def drift_qkv_f32(cfg, seed_extra: int = 0):
-    """fp32 base and direction tensors for the multi-step run:
-    step-s tensors are bf16(base + 0.05 * s * dir)."""
+    """fp32 base and direction tensors for the multi-step run (see
+    step_qkv_bits)."""
     shape = (cfg.N, cfg.heads, cfg.d)
     base = [rng(cfg.cfg_id, r, seed_extra).standard_normal(shape, dtype=np.float32)
             for r in (ROLE_Q, ROLE_K, ROLE_V)]
@@ -151,5 +151,15 @@ def drift_qkv_f32(cfg, seed_extra: int = 0):
     return base, dirs
 
 
+def step_coeffs(s: int):
+    """fp32 (cos, sin) of 0.05 s: step-s tensors rotate from base towards dir,
+    so every step's rows differ while each element stays N(0, 1), the scale
+    of normalised activations."""
+    return np.float32(np.cos(0.05 * s)), np.float32(np.sin(0.05 * s))
+
+
 def step_qkv_bits(base, dirs, s: int):
-    return tuple(f32_to_bf16_bits(b + np.float32(0.05 * s) * d) for b, d in zip(base, dirs))
+    """Step-s Q/K/V bits: bf16(cos(0.05 s) base + sin(0.05 s) dir), fp32
+    multiplies then add, rounded to nearest even."""
+    c, sn = step_coeffs(s)
+    return tuple(f32_to_bf16_bits(c * b + sn * d) for b, d in zip(base, dirs))
