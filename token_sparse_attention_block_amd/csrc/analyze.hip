@@ -364,13 +364,23 @@ __global__ __launch_bounds__(kCountThreads) void level_counts_kernel(const uint8
   const int tpbF = g.bF / g.pF, tpbH = g.bH / g.pH, tpbW = g.bW / g.pW;
   const int Ft = g.F / g.pF, Ht = g.H / g.pH, Wt = g.W / g.pW;
   uint32_t my[3] = {0u, 0u, 0u};
-  for (int b = tid; b < g.B; b += kCountThreads) {
+  // all of this thread's levels are loaded before any is used (one wait)
+  constexpr int kPer = kMaxBlocks / kCountThreads;
+  int lvr[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = tid + k * kCountThreads;
+    lvr[k] = b < g.B ? levels[b] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int b = tid + k * kCountThreads;
+    if (b >= g.B) break;
     const int bw = b % g.nBW, bh = (b / g.nBW) % g.nBH, bf = b / (g.nBW * g.nBH);
     const uint32_t tok = static_cast<uint32_t>(axis_tokens(bf, tpbF, Ft) * axis_tokens(bh, tpbH, Ht) *
                                                axis_tokens(bw, tpbW, Wt));
-    const int lv = levels[b];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) my[i] += lv == i + 1 ? tok : 0u;
+    for (int i = 0; i < 3; ++i) my[i] += lvr[k] == i + 1 ? tok : 0u;
   }
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
