@@ -334,6 +334,33 @@ def test_schedule_random_levels(torch, cfg):
         np.testing.assert_array_equal(idx.cpu().numpy()[:len(ref)], ref)
 
 
+@pytest.mark.parametrize("shape,block,patch", [
+    ((5, 4, 6, 36, 44), (2, 8, 6), (1, 2, 2)),      # blocks of 2 frames, ragged H and W edges
+    ((5, 2, 14, 42, 46), (4, 4, 4), (2, 2, 2)),     # 2x2x2 patches, 2 token frames per block, ragged
+    ((5, 2, 3, 64, 704), (1, 8, 8), (1, 2, 2)),     # 33792 tokens: 33 chunks, last one partial
+    ((5, 2, 1, 8, 8), (1, 4, 4), (1, 1, 1)),        # one chunk of 64 tokens
+], ids=["bF2-ragged", "patch222", "33-chunks", "tiny"])
+def test_schedule_grids(torch, shape, block, patch):
+    """Index lists on grids whose blocks span several token frames, with
+    ragged block edges and chunk counts that do not divide the tokens: every
+    workgroup's start offset comes out of the closed form over the blocks
+    before its chunk."""
+    K, C, F, H, W = shape
+    spec = jano.GridSpec(K, C, F, H, W, block, patch)
+    B, N = jano.grid_sizes(spec)
+    rng = np.random.default_rng(B + N)
+    lv = rng.integers(1, 4, size=B).astype(np.uint8)
+    tl = O.token_levels(lv, (F, H, W), patch, block)
+    assert tl.shape[0] == N
+    for s, periods in ((6, (4, 2, 1)), (7, (4, 2, 1)), (9, (4, 2, 1)), (2, (4, 2, 1)), (8, (3, 5, 2))):
+        for frozen in (False, True):
+            idx, n = jano.schedule(dev(lv), spec, s, 50, 5, 5, periods, frozen=frozen)
+            torch.cuda.synchronize()
+            ref = (O.schedule_frozen if frozen else O.schedule)(tl, s, 50, 5, 5, periods)
+            assert int(n.item()) == len(ref), (s, frozen)
+            np.testing.assert_array_equal(idx.cpu().numpy()[:len(ref)], ref)
+
+
 def test_check_idx(torch):
     good = dev(np.array([0, 3, 9], np.int32))
     assert int(jano.check_idx(good, 10).item()) == 0
