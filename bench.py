@@ -429,6 +429,48 @@ def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
                       "(fp64 NumPy attention; analyzer/schedule/gather/scatter excluded)" % (n_s, H, N)}
 
 
+def measure_ceilings(torch, reps=10):
+    """Ceilings re-measured on this part in this run, beside the published
+    peaks: the best of two large square bf16 GEMMs through torch.matmul (the
+    vendor GEMM library, contiguous operands) for the matrix cores, and a
+    1 GiB device-to-device copy for HBM (read + write bytes)."""
+    best, best_n = 0.0, 0
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    for n, r in ((8192, reps), (16384, max(2, reps // 4))):
+        A = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+        B = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+        C = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+        for _ in range(2):
+            torch.matmul(A, B, out=C)
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        for _ in range(r):
+            torch.matmul(A, B, out=C)
+        b.record()
+        torch.cuda.synchronize()
+        tf = 2.0 * n ** 3 * r / (a.elapsed_time(b) * 1e-3) / 1e12
+        if tf > best:
+            best, best_n = tf, n
+        del A, B, C
+    gemm = best
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    for _ in range(3):
+        y.copy_(x)
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * x.numel() * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_TFLOP/s": round(gemm, 2), "gemm_size": best_n, "copy_1GiB_GB/s": round(copy, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,6 +585,13 @@ def main():
         print("bench: 50-step interleaved run (480p)", file=sys.stderr, flush=True)
         extra["sched480p"] = sched_run(torch, jano, synth, configs.SCHED480)
 
+    print("bench: measured ceilings", file=sys.stderr, flush=True)
+    ceilings = measure_ceilings(torch)
+    ceilings["attention_frac_of_gemm"] = round(achieved / ceilings["gemm_bf16_TFLOP/s"], 4)
+    for k in ("gather", "scatter", "analyze_scores"):
+        if "GB/s" in kernels[k]:
+            ceilings["%s_frac_of_copy" % k] = round(kernels[k]["GB/s"] / ceilings["copy_1GiB_GB/s"], 4)
+
     cpu = None
     if not args.no_cpu:
         print("bench: CPU oracle sample", file=sys.stderr, flush=True)
@@ -573,6 +622,7 @@ def main():
         "step_speedup_vs_dense": speedups,
         "dense": {"ms": round(dense_ms, 4), "TFLOP/s": round(dense_tflops, 3)},
         "kernels": kernels,
+        "ceilings": ceilings,
         "writeback": writeback,
     }
     if concat is not None:
