@@ -476,6 +476,42 @@ def test_attention_peaked_and_scale(torch):
     assert_attn_close(host_bf16_f64(out), ref, "scale=0.3")
 
 
+@pytest.mark.parametrize("case", ["mid-tile", "ragged-tail", "double"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_attention_late_max_jumps(torch, d, case):
+    """The running max jumps past the rescale slack (2^8) after many tiles,
+    with N = 1000 = 15 tiles of 64 + a ragged tile of 40. Every query shares
+    a component of 4 that meets chosen keys with a large value; the other
+    components are small, so the jump is the same for every query.
+      mid-tile:    keys 448..511 (one whole tile) 8.5 log2 units up;
+      ragged-tail: keys 960..999 (the ragged tile) 8.5 log2 units up;
+      double:      key 500 up by ~20 and key 990 by ~40.
+    In the first two the keys before the jump keep a few percent of the
+    softmax weight, so a wrong rescale of what was accumulated before it
+    shows in the output."""
+    rng = np.random.default_rng(31 + d)
+    n, N, H = 100, 1000, 2
+    c = 1.4426950408889634 / np.sqrt(d)          # log2 units per unit of q . k
+    Q = 0.1 * rng.standard_normal((n, H, d)).astype(np.float32)
+    K = 0.1 * rng.standard_normal((N, H, d)).astype(np.float32)
+    V = rng.standard_normal((N, H, d)).astype(np.float32)
+    Q[:, :, 0] = 4.0
+    K[:, :, 0] = 0.0
+    up = np.float32(8.5 / (4.0 * c))
+    if case == "mid-tile":
+        K[448:512, :, 0] = up
+    elif case == "ragged-tail":
+        K[960:1000, :, 0] = up
+    else:
+        K[500, :, 0] = 40.0
+        K[990, :, 0] = 80.0
+    Qb, Kb, Vb = (synth.f32_to_bf16_bits(x) for x in (Q, K, V))
+    out = jano.attention(dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb))
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Qb), O.bf16_to_f64(Kb), O.bf16_to_f64(Vb))
+    assert_attn_close(host_bf16_f64(out), ref, "late max jump %s d=%d" % (case, d))
+
+
 def test_attention_closed_forms(torch):
     rng = np.random.default_rng(4)
     n, N, H, d = 40, 300, 2, 128
