@@ -51,7 +51,9 @@ enum {
  *                     multiple of the patch dimension.
  * Tokens form the grid (F/pF, H/pH, W/pW) in order n = (f*Ht + h)*Wt + w;
  * blocks form the grid ceil(F/bF) x ceil(H/bH) x ceil(W/bW) in order
- * b = (bf*nBH + bh)*nBW + bw (edge blocks may be ragged). */
+ * b = (bf*nBH + bh)*nBW + bw (edge blocks may be ragged). A geometry with
+ * more than 16384 blocks, or with any size below 1 (K below 3), is rejected
+ * with JANO_E_INVAL by every entry point that takes it. */
 typedef struct jano_grid {
   int32_t K, C, F, H, W;
   int32_t bF, bH, bW;

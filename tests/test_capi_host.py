@@ -77,7 +77,9 @@ def _grid(**kw):
 
 
 @pytest.mark.parametrize("kw", [dict(K=2), dict(C=0), dict(H=91), dict(bH=7), dict(pW=3),
-                                dict(bW=0), dict(F=-1)])
+                                dict(bW=0), dict(F=-1),
+                                # 4 x 64 x 65 = 16640 blocks: above the 16384-block limit
+                                dict(F=4, H=512, W=520, bF=1, bH=8, bW=8)])
 def test_bad_geometry_rejected(kw):
     L = jano.lib()
     g = _grid(**kw)
@@ -87,6 +89,15 @@ def test_bad_geometry_rejected(kw):
     fake = ctypes.c_void_p(0x1000)
     assert L.jano_analyze(fake, ctypes.byref(g), 400, 300, fake, fake, fake, fake, 1 << 30,
                           None) == jano.JANO_E_INVAL
+
+
+def test_block_limit_accepted():
+    # 128 x 128 = 16384 blocks: the largest geometry accepted
+    L = jano.lib()
+    g = _grid(F=1, H=1024, W=1024, bF=1, bH=8, bW=8)
+    B, N = ctypes.c_int64(), ctypes.c_int64()
+    assert L.jano_grid_sizes(ctypes.byref(g), ctypes.byref(B), ctypes.byref(N)) == jano.JANO_OK
+    assert B.value == 16384
 
 
 def test_analyze_argument_errors():
