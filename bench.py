@@ -12,7 +12,9 @@ One step = one pass of the whole path on resident inputs:
 by the measured wall time of the whole step. The dense reference (all N
 queries), the 10/25/50% step speedups and the 50-step interleaved run on the
 480p grid are reported beside it, as are per-kernel times from HIP events and
-the CPU oracle timed on a bounded sample.
+the CPU oracle timed on a bounded sample. Per-kernel times are medians: over
+the timed steps for gather, scatter and attention, over 200 back-to-back calls
+for the µs-scale analyzer, levels and schedule entry points.
 
     python bench.py [--steps K] [--warmup W] [--frac 0.25] [--no-cpu]
 
@@ -244,9 +246,29 @@ def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup)
         run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    per = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(STEP_CALLS)}
+    per = {k: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(STEP_CALLS)}
     per["analyze"] = per["analyze_scores"] + per["levels"]
     return p, n, wall * 1e3, per
+
+
+def time_small_calls(torch, p, reps=200):
+    """Median per-call time of the µs-scale entry points over `reps` calls
+    each. A spin kernel keeps the GPU busy while every call is enqueued with
+    its own event pair, so the calls then run back to back on the GPU and the
+    host's launch latency stays out of the intervals."""
+    calls = {"analyze_scores": lambda i: p.analyze_scores(i), "levels": lambda i: p.levels_(),
+             "schedule": lambda i: p.schedule()}
+    evs = {k: [(_ev(torch), _ev(torch)) for _ in range(reps)] for k in calls}
+    torch.cuda.synchronize()
+    torch.cuda._sleep(100_000_000)       # tens of ms of spinning on the stream
+    for i in range(reps):
+        for k, call in calls.items():
+            a, b = evs[k][i]
+            a.record()
+            call(i)
+            b.record()
+    torch.cuda.synchronize()
+    return {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in evs.items()}
 
 
 def time_writeback(torch, jano, cfg, idx, reps=20):
@@ -494,7 +516,7 @@ def measure_ceilings(torch, reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--frac", type=float, default=0.25)
     ap.add_argument("--no-cpu", action="store_true")
@@ -539,6 +561,9 @@ def main():
     print("bench: headline fraction %.2f" % args.frac, file=sys.stderr, flush=True)
     p, n_act, ms_step, per = time_fraction(torch, jano, synth, cfg, args.frac, Q, K, V, Kc, Vc,
                                            args.steps, args.warmup)
+    small = time_small_calls(torch, p)
+    per.update(small)
+    per["analyze"] = per["analyze_scores"] + per["levels"]
     attn_flops = 4.0 * n_act * N * H * d
     value = attn_flops / (ms_step * 1e-3) / 1e12
     achieved = attn_flops / (per["attention"] * 1e-3) / 1e12
