@@ -465,8 +465,18 @@ def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
         O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
         t = time.perf_counter() - t0
     flops = 4.0 * n_s * N * H * d
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(t, 2),
+            "kind": "oracle", "seconds": round(t, 2), "cpu_model": model,
+            "host_cpus": os.cpu_count(),
             "sample": "%d active queries x %d heads against the full %d-token K/V cache "
                       "(fp64 NumPy attention; analyzer/schedule/gather/scatter excluded)" % (n_s, H, N)}
 
