@@ -540,7 +540,7 @@ def main():
         ingest_counters(*args.ingest_counters, "720p-active%d" % round(100 * args.frac))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the path has no multi-GPU mode "
               "(heads would shard across GPUs with no exchange inside the path)", file=sys.stderr)
         sys.exit(2)
     if args.frac not in MIX_FOR_ACTIVE:
