@@ -173,35 +173,55 @@ __global__ __launch_bounds__(kPW * kWave) void qkv_proj_kernel(
   }
   if (t < nk) mfmas(fa0, fb0);
 
-  // epilogue: lane holds columns n .. n+3 of token m for every (nt, mt)
+  // epilogue: lane holds columns n .. n+3 of token m for every (nt, mt).
+  // What depends only on the column -- output part, head column, and each
+  // rotary pair's axis and frequency (in turns per position) -- is worked
+  // out once per column tile; per token only the angle is formed, reduced
+  // to [0, 1) turns and fed to the hardware sine and cosine (v_sin_f32 /
+  // v_cos_f32 take turns).
+  constexpr float kInv2Pi = 0.15915494309189535f;
+  int part_of[8], col_of[8], ax_of[8][2];
+  float turns_of[8][2];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int n = n0 + 128 * wn + 16 * nt + 4 * h4;
+    part_of[nt] = n / g.HD;
+    col_of[nt] = n % g.HD;
+    const int j0 = col_of[nt] % g.d;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j = j0 + 2 * p;
+      int ax, i, mm;
+      if (j < g.df) {
+        ax = 0; i = j / 2; mm = g.df;
+      } else if (j < g.df + g.dh) {
+        ax = 1; i = (j - g.df) / 2; mm = g.dh;
+      } else {
+        ax = 2; i = (j - g.df - g.dh) / 2; mm = g.dh;
+      }
+      ax_of[nt][p] = ax;
+      turns_of[nt][p] = exp2f(-(2.0f * i / mm) * g.log2_base) * kInv2Pi;
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int m = m0 + 64 * wm + 16 * mt + l16;
     if (m >= g.n_act) continue;
     const int tok = idx[m];
-    const int pos[3] = {tok / (g.Ht * g.Wt), (tok / g.Wt) % g.Ht, tok % g.Wt};
+    const float pos[3] = {static_cast<float>(tok / (g.Ht * g.Wt)), static_cast<float>((tok / g.Wt) % g.Ht),
+                          static_cast<float>(tok % g.Wt)};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int n = n0 + 128 * wn + 16 * nt + 4 * h4;
       if (n >= g.Nout) continue;
-      const int part = n / g.HD, col = n % g.HD;
+      const int part = part_of[nt], col = col_of[nt];
       float v[4] = {acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
       if (part < 2 && g.rope) {
-        const int j0 = col % g.d;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int j = j0 + 2 * p;
-          int ax, i, mm;
-          if (j < g.df) {
-            ax = 0; i = j / 2; mm = g.df;
-          } else if (j < g.df + g.dh) {
-            ax = 1; i = (j - g.df) / 2; mm = g.dh;
-          } else {
-            ax = 2; i = (j - g.df - g.dh) / 2; mm = g.dh;
-          }
-          const float theta = exp2f(-(2.0f * i / mm) * g.log2_base);
-          float sn, cs;
-          sincosf(static_cast<float>(pos[ax]) * theta, &sn, &cs);
+          const float t = pos[ax_of[nt][p]] * turns_of[nt][p];
+          const float r = t - floorf(t);
+          const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
           const float x0 = v[2 * p], x1 = v[2 * p + 1];
           v[2 * p] = x0 * cs - x1 * sn;
           v[2 * p + 1] = x0 * sn + x1 * cs;
