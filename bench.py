@@ -66,7 +66,7 @@ def _short_kernel_name(name):
     return name.split("(")[0].split("<")[0]
 
 
-def ingest_counters(fetch_path, write_path, workload):
+def ingest_counters(fetch_path, write_path, workload, out_path=None):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) -> HBM bytes per launch.
 
     Each counter is scaled by what it reads for the 1 GiB device copy that
@@ -130,7 +130,7 @@ def ingest_counters(fetch_path, write_path, workload):
             out[name] = {"source": src, "source_sha256_16": kernel_source_hash(src),
                          "grid_threads": g, "fetch_bytes": round(fb), "write_bytes": round(wb),
                          "hbm_bytes_per_launch": round(fb + wb)}
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    p = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     allw = {}
     if os.path.exists(p):
         with open(p) as f:
@@ -140,12 +140,13 @@ def ingest_counters(fetch_path, write_path, workload):
         json.dump(allw, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(out, indent=1))
+    return out
 
 
-def load_traffic(key, workload):
+def load_traffic(key, workload, path=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary, only
     if it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    p = path or os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
