@@ -507,6 +507,7 @@ def measure_ceilings(torch, reps=10):
             best, best_n = tf, n
         del A, B, C
     gemm = best
+    loop = measure_mfma_loop(torch)
     x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     x.fill_(1.0)
@@ -521,7 +522,45 @@ def measure_ceilings(torch, reps=10):
     copy = 2.0 * x.numel() * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
     del x, y
     torch.cuda.empty_cache()
-    return {"gemm_bf16_TFLOP/s": round(gemm, 2), "gemm_size": best_n, "copy_1GiB_GB/s": round(copy, 1)}
+    out = {"gemm_bf16_TFLOP/s": round(gemm, 2), "gemm_size": best_n, "copy_1GiB_GB/s": round(copy, 1)}
+    out.update(loop)
+    return out
+
+
+def measure_mfma_loop(torch, iters=30000):
+    """The bf16 matrix-core rate this part sustains under full load: the
+    calibration library's register-only MFMA loop (no memory traffic, no other
+    instructions) on one workgroup of 8 waves per CU, timed with events, for
+    both MFMA shapes; also the shader clock each ran at (a wave's loop cycles
+    over the launch time)."""
+    import ctypes
+    from token_sparse_attention_block_amd import build as B
+    if not os.path.exists(B.CALIB_LIB):
+        raise RuntimeError("%s is not built (run __graft_entry__.build())" % B.CALIB_LIB)
+    f = ctypes.CDLL(B.CALIB_LIB).jano_calib_mfma_loop
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(ncu * 512, dtype=torch.float32, device="cuda")
+    cyc = torch.empty(ncu * 8, dtype=torch.int64, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        if f(shape, ncu, 500, ctypes.c_void_p(sink.data_ptr()), None, st) != 0:
+            raise RuntimeError("jano_calib_mfma_loop failed")
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        rc = f(shape, ncu, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(cyc.data_ptr()), st)
+        b.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError("jano_calib_mfma_loop failed")
+        ms = a.elapsed_time(b)
+        flop = ncu * 8 * iters * 524288.0
+        res["mfma_loop_%s_TFLOP/s" % name] = round(flop / (ms * 1e-3) / 1e12, 2)
+        res["mfma_loop_%s_GHz" % name] = round(float(cyc.max().item()) / (ms * 1e-3) / 1e9, 3)
+    res["mfma_loop_bf16_TFLOP/s"] = max(res["mfma_loop_16x16x32_TFLOP/s"], res["mfma_loop_32x32x16_TFLOP/s"])
+    return res
 
 
 def main():
@@ -644,6 +683,7 @@ def main():
     print("bench: measured ceilings", file=sys.stderr, flush=True)
     ceilings = measure_ceilings(torch)
     ceilings["attention_frac_of_gemm"] = round(achieved / ceilings["gemm_bf16_TFLOP/s"], 4)
+    ceilings["attention_frac_of_mfma_loop"] = round(achieved / ceilings["mfma_loop_bf16_TFLOP/s"], 4)
     for k in ("gather", "scatter", "analyze_scores"):
         if "GB/s" in kernels[k]:
             ceilings["%s_frac_of_copy" % k] = round(kernels[k]["GB/s"] / ceilings["copy_1GiB_GB/s"], 4)

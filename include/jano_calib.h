@@ -1,0 +1,35 @@
+/* Calibration aid for measurements (not part of the Jano path).
+ *
+ * jano_calib_mfma_loop launches `workgroups` workgroups of 512 threads
+ * (8 waves, two per SIMD, one workgroup per CU) that each run `iters`
+ * iterations of a register-only loop of independent bf16 MFMAs, 524288 flop
+ * per wave per iteration: shape 0 uses v_mfma_f32_16x16x32_bf16, shape 1
+ * v_mfma_f32_32x32x16_bf16. Timed with events on `stream`, it gives the
+ * matrix-core rate the part sustains under full load, a measured ceiling to
+ * set beside the published peak.
+ *
+ *   sink    device buffer of workgroups * 512 floats; written only in a case
+ *           that does not occur (it keeps the loop from being removed)
+ *   cycles  NULL, or a device buffer of workgroups * 8 int64 that receives
+ *           each wave's shader-clock cycles for its loop
+ *   stream  hipStream_t, or NULL for the default stream
+ *
+ * Returns 0 on success, 1 for a bad argument (shape not 0 or 1, workgroups or
+ * iters < 1, sink NULL; nothing is launched), 2 when the launch fails.
+ * Buffers belong to the caller. The call is asynchronous.
+ */
+#ifndef JANO_CALIB_H
+#define JANO_CALIB_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int jano_calib_mfma_loop(int shape, int workgroups, int iters, float *sink, long long *cycles,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JANO_CALIB_H */

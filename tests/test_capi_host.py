@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI: the library loads, exports every function
-include/jano.h declares, and rejects bad arguments before touching a GPU.
-No kernel is launched here (runs on machines without a GPU)."""
+include/jano.h declares, and rejects bad arguments before touching a GPU; the
+calibration library exports what include/jano_calib.h declares and rejects
+bad arguments. No kernel is launched here (runs on machines without a GPU)."""
 import ctypes
 import os
 import re
@@ -17,8 +18,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(jano.LIB_PATH),
                                 reason="libjano.so not built (run __graft_entry__.build())")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(jano_[a-z_0-9]+)\s*\(",
                                  src, flags=re.M)))
 
@@ -36,6 +37,26 @@ def test_library_exports_every_declared_symbol():
     L = jano.lib()
     for name in declared_functions():
         assert hasattr(L, name)
+
+
+def test_calib_library_exports_and_rejects():
+    from token_sparse_attention_block_amd import build as B
+    names = declared_functions(os.path.join(ROOT, "include", "jano_calib.h"))
+    assert names == ["jano_calib_mfma_loop"]
+    out = subprocess.run(["nm", "-D", "--defined-only", B.CALIB_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert set(names) <= syms
+    f = ctypes.CDLL(B.CALIB_LIB).jano_calib_mfma_loop
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    sink = ctypes.c_void_p(0x1000)   # never dereferenced: every call below is rejected first
+    assert f(2, 1, 1, sink, None, None) == 1
+    assert f(-1, 1, 1, sink, None, None) == 1
+    assert f(0, 0, 1, sink, None, None) == 1
+    assert f(0, 1, 0, sink, None, None) == 1
+    assert f(1, 1, 1, None, None, None) == 1
 
 
 def test_version_and_status_strings():

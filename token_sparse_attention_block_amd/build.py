@@ -1,9 +1,11 @@
-"""Builds libjano.so (HIP for gfx950) in-tree with hipcc.
+"""Builds libjano.so (HIP for gfx950) in-tree with hipcc, and beside it
+libjano_calib.so, the calibration kernel that measurements use to find the
+matrix-core rate the part sustains (not part of the Jano path).
 
     python -m token_sparse_attention_block_amd.build [-v]
 
-Objects go to token_sparse_attention_block_amd/_build/, the library to
-token_sparse_attention_block_amd/lib/libjano.so (replaced atomically).
+Objects go to token_sparse_attention_block_amd/_build/, the libraries to
+token_sparse_attention_block_amd/lib/ (each replaced atomically).
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ OBJ = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libjano.so")
 SOURCES = ["capi.hip", "analyze.hip", "schedule.hip", "rows.hip", "attention.hip", "proj.hip"]
+CALIB_LIB = os.path.join(LIBDIR, "libjano_calib.so")
+CALIB_SOURCES = ["calib/mfma_loop.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -57,17 +61,19 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cc = hipcc()
     os.makedirs(OBJ, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    objs = []
+    libs = ((LIB, SOURCES), (CALIB_LIB, CALIB_SOURCES))
     cmds = []
-    for s in SOURCES:
-        o = os.path.join(OBJ, s.replace(".hip", ".o"))
-        objs.append(o)
-        cmds.append([cc] + COMMON + EXTRA.get(s, []) + ["-c", os.path.join(SRC, s), "-o", o])
+    for _, sources in libs:
+        for s in sources:
+            o = os.path.join(OBJ, s.replace("/", "_").replace(".hip", ".o"))
+            cmds.append([cc] + COMMON + EXTRA.get(s, []) + ["-c", os.path.join(SRC, s), "-o", o])
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
+    for lib, sources in libs:
+        objs = [os.path.join(OBJ, s.replace("/", "_").replace(".hip", ".o")) for s in sources]
+        tmp = lib + ".tmp"
+        _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
