@@ -126,6 +126,43 @@ def analyze_scores_bruteforce(lat: np.ndarray, block) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FFT complexity baseline: an alternative index source, not the method.
+# Jano pages: [fr] §2.A (frequency measures such as the FFT, which the
+# analyzer replaces because they are unreliable on noisy early latents);
+# [zh] §2.1 (the comparison: an FFT computed directly on the early latents);
+# [pt] results (the baseline's recognition accuracy beside the analyzer's).
+# The pages give no formula. Reading taken: per block and channel, the energy
+# of the block's 3D DFT outside the DC term, over the latest warm-up latent
+# L[K-1], divided by n^2 (n = the block's pixels inside the latent), averaged
+# over the channels.
+# --------------------------------------------------------------------------
+
+def fft_block_scores_f64(lat: np.ndarray, block) -> np.ndarray:
+    """FFT-baseline score per block, fp64 [B]. lat: fp32 [K, C, F, H, W]."""
+    K, C, F, H, W = lat.shape
+    L = np.asarray(lat[K - 1], dtype=np.float64)          # [C, F, H, W]
+    bF, bH, bW = block
+    nB = block_grid(F, H, W, block)
+    out = np.zeros(nB[0] * nB[1] * nB[2], dtype=np.float64)
+    b = 0
+    for bf in range(nB[0]):
+        for bh in range(nB[1]):
+            for bw in range(nB[2]):
+                x = L[:, bf * bF:(bf + 1) * bF, bh * bH:(bh + 1) * bH, bw * bW:(bw + 1) * bW]
+                n = x[0].size
+                X = np.fft.fftn(x, axes=(1, 2, 3))
+                energy = (np.abs(X) ** 2).reshape(C, -1)
+                out[b] = energy[:, 1:].sum(axis=1).mean() / float(n) ** 2   # [:, 0] is DC
+                b += 1
+    return out
+
+
+def fft_block_scores(lat: np.ndarray, block) -> np.ndarray:
+    """fft_block_scores_f64 rounded to fp32 [B]."""
+    return fft_block_scores_f64(lat, block).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
 # Levels. Jano pages: [nl] methodology §1 (three convergence levels:
 # Static, Moderate, Active); [zh] §2.2 item 1; [ko] §2.B.
 # --------------------------------------------------------------------------

@@ -135,6 +135,83 @@ def test_signal_variant_ranks_textured_blocks_on_top():
     assert set(np.flatnonzero(lv == 3)) == set(np.flatnonzero(tex))
 
 
+# ----------------------------------------------- FFT complexity baseline --
+
+def _block_variance_direct(lat, block):
+    """Mean over channels of each block's population variance of the last
+    latent, by plain loops (no DFT)."""
+    K, C, F, H, W = lat.shape
+    L = lat[K - 1].astype(np.float64)
+    bF, bH, bW = block
+    out = []
+    for bf in range(-(-F // bF)):
+        for bh in range(-(-H // bH)):
+            for bw in range(-(-W // bW)):
+                v = []
+                for c in range(C):
+                    x = L[c, bf * bF:(bf + 1) * bF, bh * bH:(bh + 1) * bH, bw * bW:(bw + 1) * bW].ravel()
+                    m = sum(x) / len(x)
+                    v.append(sum((xi - m) ** 2 for xi in x) / len(x))
+                out.append(sum(v) / C)
+    return np.array(out)
+
+
+def test_fft_scores_equal_block_variance():
+    # Parseval: the DFT energy outside the DC term over n^2 is the population
+    # variance; ragged edge blocks use the pixels present
+    rng = np.random.default_rng(7)
+    for shape, block in [((3, 2, 3, 10, 13), (2, 4, 5)), ((4, 3, 1, 9, 9), (1, 4, 4)),
+                         ((3, 1, 5, 6, 7), (3, 3, 3))]:
+        lat = (3.0 * rng.standard_normal(shape) + 1.0).astype(np.float32)
+        np.testing.assert_allclose(O.fft_block_scores_f64(lat, block),
+                                   _block_variance_direct(lat, block), rtol=1e-12, atol=1e-14)
+
+
+def test_fft_scores_closed_forms():
+    h = np.arange(8.0)[:, None]
+    w = np.arange(8.0)[None, :]
+    lat = np.zeros((3, 3, 1, 8, 8))
+    lat[2, 0, 0] = 3.0 * np.cos(2 * np.pi * (h / 8 + 2 * w / 8)) + 5.0   # variance 9/2, DC ignored
+    lat[2, 1, 0] = 2.0 * np.cos(2 * np.pi * 3 * w / 8)                   # variance 4/2
+    lat[2, 2, 0] = 0.5 * np.cos(np.pi * h)                               # Nyquist: variance 1/4
+    lat[0] = 100.0                                                       # earlier latents ignored
+    s = O.fft_block_scores_f64(lat.astype(np.float32), (1, 8, 8))
+    assert s.shape == (1,)
+    assert abs(s[0] - (4.5 + 2.0 + 0.25) / 3) <= 1e-6
+    const = np.full((3, 2, 2, 8, 8), 0.37, dtype=np.float32)
+    assert np.all(np.abs(O.fft_block_scores_f64(const, (1, 4, 4))) <= 1e-20)
+
+
+def test_fft_scores_last_latent_scale_and_offset():
+    rng = np.random.default_rng(11)
+    lat = rng.standard_normal((4, 2, 2, 8, 12)).astype(np.float32)
+    block = (1, 4, 4)
+    base = O.fft_block_scores_f64(lat, block)
+    other = lat.copy()
+    other[:-1] = rng.standard_normal(other[:-1].shape)
+    np.testing.assert_array_equal(O.fft_block_scores_f64(other, block), base)
+    np.testing.assert_allclose(O.fft_block_scores_f64(lat * np.float32(4.0), block), 16.0 * base,
+                               rtol=1e-12)
+    shifted = lat.astype(np.float64)                                     # exact offsets
+    offs = rng.integers(-8, 8, size=(2, 2, 2, 3)).astype(np.float64)     # one constant per block
+    shifted[-1] += np.repeat(np.repeat(offs, 4, axis=2), 4, axis=3)
+    np.testing.assert_allclose(O.fft_block_scores_f64(shifted, block), base, rtol=1e-9, atol=1e-12)
+
+
+def test_fft_baseline_misses_textured_blocks_on_noisy_latents():
+    # On the signal variant (textured blocks quadratic in the step) the
+    # analyzer's Active set is exactly the textured blocks, while the FFT
+    # baseline on the latest, still noise-dominated latent recovers only about
+    # half of them -- the behaviour the pages' comparison describes.
+    cfg = configs.IMAGE
+    lat = synth.latents(cfg, signal=True)
+    tex = set(np.flatnonzero(synth.texture_blocks(cfg).ravel()))
+    act_an = set(np.flatnonzero(O.assign_levels(O.analyze_scores(lat, cfg.block)) == 3))
+    act_fft = set(np.flatnonzero(O.assign_levels(O.fft_block_scores(lat, cfg.block)) == 3))
+    assert act_an == tex
+    assert len(act_fft & tex) < 0.75 * len(tex)
+
+
 # ------------------------------------------------------------------ levels --
 
 def test_level_split_counts():
