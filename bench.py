@@ -14,7 +14,8 @@ queries), the 10/25/50% step speedups and the 50-step interleaved run on the
 480p grid are reported beside it, as are per-kernel times from HIP events and
 the CPU oracle timed on a bounded sample. Per-kernel times are medians: over
 the timed steps for gather, scatter and attention, over 200 back-to-back calls
-for the µs-scale analyzer, levels and schedule entry points.
+for the µs-scale analyzer, levels, schedule and FFT-baseline score entry
+points.
 
     python bench.py [--steps K] [--warmup W] [--frac 0.25] [--no-cpu]
 
@@ -160,7 +161,7 @@ def load_traffic(key, workload, path=None):
 class Path:
     """Device-resident inputs and outputs of one workload."""
 
-    def __init__(self, torch, jano, synth, cfg, frac, n_lat_copies=3):
+    def __init__(self, torch, jano, synth, cfg, frac, n_lat_copies=5):
         self.torch, self.jano, self.cfg, self.frac = torch, jano, cfg, frac
         dev = "cuda"
         self.spec = jano.GridSpec.of(cfg)
@@ -172,6 +173,7 @@ class Path:
         B, N = jano.grid_sizes(self.spec)
         self.B, self.N = B, N
         self.scores = torch.empty(B, dtype=torch.float32, device=dev)
+        self.fft = torch.empty(B, dtype=torch.float32, device=dev)
         self.levels = torch.empty(B, dtype=torch.uint8, device=dev)
         self.counts = torch.empty(3, dtype=torch.int32, device=dev)
         self.ws = torch.empty(jano.analyze_workspace_bytes(self.spec), dtype=torch.uint8, device=dev)
@@ -192,6 +194,10 @@ class Path:
 
     def analyze_scores(self, i):
         self.jano.analyze_scores(self.lats[i % len(self.lats)], self.spec, self.scores, self.ws)
+
+    def fft_scores(self, i):
+        # the copy the analyzer read longest ago, so it streams from HBM too
+        self.jano.fft_scores(self.lats[(i + 1) % len(self.lats)], self.spec, self.fft)
 
     def levels_(self):
         self.jano.levels(self.scores, self.spec, self.spm, self.mpm, self.levels, self.counts)
@@ -258,7 +264,7 @@ def time_small_calls(torch, p, reps=200):
     its own event pair, so the calls then run back to back on the GPU and the
     host's launch latency stays out of the intervals."""
     calls = {"analyze_scores": lambda i: p.analyze_scores(i), "levels": lambda i: p.levels_(),
-             "schedule": lambda i: p.schedule()}
+             "schedule": lambda i: p.schedule(), "fft_scores": lambda i: p.fft_scores(i)}
     evs = {k: [(_ev(torch), _ev(torch)) for _ in range(reps)] for k in calls}
     torch.cuda.synchronize()
     torch.cuda._sleep(100_000_000)       # tens of ms of spinning on the stream
@@ -618,6 +624,7 @@ def main():
     value = attn_flops / (ms_step * 1e-3) / 1e12
     achieved = attn_flops / (per["attention"] * 1e-3) / 1e12
     lat_bytes = cfg.latent_bytes + p.B * 4      # latents read, scores written
+    fft_bytes = cfg.latent_bytes // cfg.K + p.B * 4   # the latest latent read, scores written
     row_bytes = H * d * 2
     kernels = {
         "analyze_scores": {"ms": per["analyze_scores"], "bytes": lat_bytes,
@@ -630,8 +637,11 @@ def main():
         "scatter": {"ms": per["scatter"], "bytes": 4 * n_act * row_bytes,
                     "GB/s": 4 * n_act * row_bytes / (per["scatter"] * 1e-3) / 1e9},
         "attention": {"ms": per["attention"], "flops": attn_flops, "TFLOP/s": achieved},
+        "fft_scores": {"ms": per["fft_scores"], "bytes": fft_bytes,
+                       "GB/s": fft_bytes / (per["fft_scores"] * 1e-3) / 1e9},
     }
     wl = "720p-active%d" % round(100 * args.frac)
+    kernels["fft_scores"]["frac_hbm"] = kernels["fft_scores"]["GB/s"] / PEAK_HBM_GBS
     for k in ("analyze_scores", "gather", "scatter"):
         kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / PEAK_HBM_GBS
         kernels[k]["traffic"] = load_traffic("analyze_stream" if k == "analyze_scores" else k, wl)

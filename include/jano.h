@@ -102,6 +102,26 @@ int jano_analyze_scores(const float *lat, const jano_grid *g, float *scores, voi
                         size_t ws_bytes, void *stream);
 
 /*
+ * jano_fft_scores -- the FFT complexity baseline, an alternative index source.
+ * Pages: fr §2.A (frequency measures such as the FFT, which the analyzer
+ * replaces because they are unreliable on noisy early latents); zh §2.1 (the
+ * comparison: an FFT taken directly on the early latents); pt results. The
+ * pages give no formula; the measure taken is the energy of each block's 3D
+ * DFT outside the DC term, divided by n^2, averaged over the channels.
+ *
+ *   lat               [K][C][F][H][W] fp32 (finite values); only the latest
+ *                     latent, L[K-1], is read
+ *   scores   (out)    [B] fp32: per block, the mean over channels of
+ *                     sum_{k != 0} |DFT(L[K-1][c] restricted to the block)_k|^2 / n^2
+ *                     with n the block's pixels inside the latent -- by
+ *                     Parseval the population variance of those pixels, which
+ *                     is what is computed (two passes in fp64)
+ * Rank the scores with jano_levels exactly as the analyzer's. No workspace.
+ * Deterministic. Errors: JANO_E_INVAL for null pointers or a bad grid.
+ */
+int jano_fft_scores(const float *lat, const jano_grid *g, float *scores, void *stream);
+
+/*
  * jano_levels -- level bucketing of block scores.
  * Pages: nl methodology §1 (three convergence levels: static, moderate,
  * active); zh §2.1.

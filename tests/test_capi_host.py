@@ -145,6 +145,11 @@ def test_analyze_argument_errors():
     assert L.jano_levels(fake, ctypes.byref(g), 400, -1, fake, fake, None) == -1
     bad = _grid(K=2)
     assert L.jano_levels(fake, ctypes.byref(bad), 400, 300, fake, fake, None) == -1
+    # the FFT-baseline index source
+    assert L.jano_fft_scores(null, ctypes.byref(g), fake, None) == -1
+    assert L.jano_fft_scores(fake, ctypes.byref(g), null, None) == -1
+    assert L.jano_fft_scores(fake, ctypes.byref(bad), fake, None) == -1
+    assert L.jano_fft_scores(fake, None, fake, None) == -1
 
 
 def test_schedule_argument_errors():

@@ -169,6 +169,60 @@ def test_analyzer_closed_forms(torch, golden):
     np.testing.assert_array_equal(s, expect)
 
 
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.IMAGE, configs.V480, configs.V720],
+                         ids=lambda c: c.name)
+@pytest.mark.parametrize("signal", [False, True], ids=["literal", "signal"])
+def test_fft_scores_configs(torch, cfg, signal):
+    # the FFT-baseline index source: scores against the oracle's DFT energies,
+    # then its levels through jano_levels, and one interleaved step's index list
+    print("fft scores", cfg.name, signal, flush=True)
+    lat = synth.latents(cfg, signal=signal)
+    spec = jano.GridSpec.of(cfg)
+    s = jano.fft_scores(dev(lat), spec)
+    lv, cnt = jano.levels(s, spec, cfg.static_permille, cfg.moderate_permille)
+    torch.cuda.synchronize()
+    ref64 = O.fft_block_scores_f64(lat, spec.block)
+    got = s.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref64)
+    bad = err > SCORE_RTOL * np.abs(ref64)
+    assert not bad.any(), ("scores", int(bad.sum()), float(err[bad].max()))
+    ref32 = ref64.astype(np.float32)
+    lv_ref = O.assign_levels(ref32, cfg.static_permille, cfg.moderate_permille)
+    band = threshold_band(ref32, cfg.static_permille, cfg.moderate_permille)
+    l_gpu = lv.cpu().numpy()
+    assert not ((l_gpu != lv_ref) & ~band).any()
+    fhw = (spec.F, spec.H, spec.W)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), O.level_token_counts(l_gpu, fhw, spec.patch, spec.block))
+    sc = cfg.schedule
+    step = sc.W + 1
+    idx, n_dev = jano.schedule(lv, spec, step, sc.T, sc.W, sc.Cd, sc.periods)
+    torch.cuda.synchronize()
+    ref_idx = O.schedule(O.token_levels(l_gpu, fhw, spec.patch, spec.block), step, sc.T, sc.W, sc.Cd,
+                         sc.periods)
+    n = int(n_dev.item())
+    assert n == len(ref_idx)
+    np.testing.assert_array_equal(idx[:n].cpu().numpy(), ref_idx)
+    print("  blocks in threshold band:", int(band.sum()), " n_act at step", step, ":", n, flush=True)
+
+
+@pytest.mark.parametrize("shape,block", [
+    ((3, 2, 3, 10, 13), (2, 4, 5)),        # ragged edges along every axis
+    ((4, 3, 1, 9, 9), (1, 4, 4)),
+    ((3, 5, 2, 8, 2100), (1, 8, 1)),       # 2100 block columns: two column passes
+    ((3, 1, 1, 4, 4), (1, 4, 4)),          # one block
+    ((3, 2, 2, 9, 20), (1, 4, 8)),         # 16-byte loads, ragged last block column and row
+])
+def test_fft_scores_shapes(torch, shape, block):
+    print("fft scores shape", shape, block, flush=True)
+    rng = np.random.default_rng(sum(shape))
+    lat = (2.0 * rng.standard_normal(shape) + 3.0).astype(np.float32)
+    spec = jano.GridSpec(*shape, block=block, patch=(1, 1, 1))
+    s = jano.fft_scores(dev(lat), spec)
+    torch.cuda.synchronize()
+    ref64 = O.fft_block_scores_f64(lat, block)
+    np.testing.assert_allclose(s.cpu().numpy().astype(np.float64), ref64, rtol=SCORE_RTOL, atol=0)
+
+
 @pytest.mark.parametrize("spm,mpm", [(0, 0), (1000, 0), (0, 1000), (400, 600), (333, 333)])
 def test_analyzer_level_mixes(torch, spm, mpm):
     cfg = configs.TINY

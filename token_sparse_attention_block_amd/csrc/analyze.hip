@@ -29,6 +29,9 @@
 // fixed order, divides by the closed-form term count and rounds the score to
 // fp32. Kernels 1 and 2 are jano_analyze_scores.
 //
+// The FFT complexity baseline (jano_fft_scores, an alternative index source
+// whose scores go through the same levels) is fft_scores_kernel.
+//
 // Levels (jano_levels): kernel 3 (rank_levels_kernel) gives every block its
 // exact rank in the (score, block id) order and the level that rank falls in;
 // kernel 4 (level_counts_kernel, one workgroup) counts the tokens of each
@@ -413,6 +416,90 @@ hipError_t launch_stream_r(const float *lat, const AnalyzeGeom &g, double *part,
   }
 }
 
+// ---------------------------------------------------------------------------
+// FFT complexity baseline (jano_fft_scores), an alternative index source.
+// Per block: the energy of the block's 3D DFT outside the DC term, of the
+// latest warm-up latent, over n^2 (n = the block's pixels inside the latent),
+// averaged over the channels. By Parseval that quantity is the block's
+// population variance, so the kernel takes the variance directly, no
+// transform: one pass of fp64 sums of (x - x0) and (x - x0)^2, with x0 the
+// block's first value (shifting by a value of the block keeps the difference
+// of the two sums well conditioned, and a constant block gives exactly 0).
+// One workgroup per block row (bf, bh); threads run over (channel, block
+// column) pairs with the column fastest, so neighbouring lanes read
+// neighbouring 16-byte pieces of one latent row (VEC: bW a multiple of 4,
+// 16-byte aligned rows). Each block's channel sum is taken in channel order
+// from LDS, so the result is deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kFftThreads = 256;
+constexpr int kFftCols = 1024;             // block columns per pass over a block row
+constexpr int kFftPairs = 2048;            // (channel, block column) variances held in LDS
+
+template <bool VEC>
+__global__ __launch_bounds__(kFftThreads) void fft_scores_kernel(const float *__restrict__ lat,
+                                                                  AnalyzeGeom g,
+                                                                  float *__restrict__ scores) {
+  __shared__ double var[kFftPairs];
+  __shared__ double acc[kFftCols];
+  const int brow = blockIdx.x;                       // bf * nBH + bh
+  const int bf = brow / g.nBH, bh = brow % g.nBH;
+  const int f0 = bf * g.bF, f1 = min(g.F, f0 + g.bF);
+  const int h0 = bh * g.bH, h1 = min(g.H, h0 + g.bH);
+  const size_t plane = static_cast<size_t>(g.H) * g.W;
+  const float *L = lat + static_cast<size_t>(g.K - 1) * g.C * g.F * plane;
+  for (int bw0 = 0; bw0 < g.nBW; bw0 += kFftCols) {
+    const int nw = min(kFftCols, g.nBW - bw0);
+    for (int j = threadIdx.x; j < nw; j += kFftThreads) acc[j] = 0.0;
+    const int cpp = kFftPairs / nw;                  // channels per pass (>= 2)
+    for (int c0 = 0; c0 < g.C; c0 += cpp) {
+      const int cn = min(cpp, g.C - c0);
+      __syncthreads();                               // the previous pass's var reads are done
+      for (int p = threadIdx.x; p < cn * nw; p += kFftThreads) {
+        const int c = c0 + p / nw, bw = bw0 + p % nw;
+        const int w0 = bw * g.bW, w1 = min(g.W, w0 + g.bW);
+        const float *Lc = L + static_cast<size_t>(c) * g.F * plane + static_cast<size_t>(h0) * g.W + w0;
+        const double x0 = static_cast<double>(Lc[static_cast<size_t>(f0) * plane]);
+        double s1 = 0.0, s2 = 0.0;
+        for (int f = f0; f < f1; ++f) {
+#pragma unroll 4
+          for (int h = 0; h < h1 - h0; ++h) {
+            const float *row = Lc + f * plane + static_cast<size_t>(h) * g.W;
+            if constexpr (VEC) {
+              // bW a multiple of 4 and rows 16-byte aligned; a ragged last
+              // block still ends on a multiple of 4 because W is one too
+              for (int w = 0; w < w1 - w0; w += 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(row + w);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const double d = static_cast<double>(v[e]) - x0;
+                  s1 += d;
+                  s2 += d * d;
+                }
+              }
+            } else {
+              for (int w = 0; w < w1 - w0; ++w) {
+                const double d = static_cast<double>(row[w]) - x0;
+                s1 += d;
+                s2 += d * d;
+              }
+            }
+          }
+        }
+        const double n = static_cast<double>((f1 - f0) * (h1 - h0) * (w1 - w0));
+        var[p] = fmax(s2 - s1 * (s1 / n), 0.0) / n;
+      }
+      __syncthreads();
+      for (int j = threadIdx.x; j < nw; j += kFftThreads) {
+        double a = acc[j];
+        for (int cc = 0; cc < cn; ++cc) a += var[cc * nw + j];
+        acc[j] = a;                                  // only this thread touches acc[j]
+      }
+    }
+    for (int j = threadIdx.x; j < nw; j += kFftThreads)
+      scores[static_cast<size_t>(brow) * g.nBW + bw0 + j] = static_cast<float>(acc[j] / g.C);
+  }
+}
+
 }  // namespace
 
 bool analyze_plan(int K, int C, int F, int H, int W, int bF, int bH, int bW, int pF, int pH,
@@ -475,6 +562,16 @@ hipError_t launch_analyze_scores(const float *lat, const AnalyzeGeom &g, float *
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(block_scores_kernel, dim3((g.B + 255) / 256), dim3(256), 0, s, part, g, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_fft_scores(const float *lat, const AnalyzeGeom &g, float *scores, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(g.nBF * g.nBH));
+  const bool vec = g.bW % 4 == 0 && g.W % 4 == 0 && reinterpret_cast<uintptr_t>(lat) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(fft_scores_kernel<true>, grid, dim3(kFftThreads), 0, s, lat, g, scores);
+  else
+    hipLaunchKernelGGL(fft_scores_kernel<false>, grid, dim3(kFftThreads), 0, s, lat, g, scores);
   return hipGetLastError();
 }
 

@@ -125,6 +125,13 @@ int jano_analyze_scores(const float *lat, const jano_grid *g, float *scores, voi
   return hip_status(jano::launch_analyze_scores(lat, a, scores, ws, static_cast<hipStream_t>(stream)));
 }
 
+int jano_fft_scores(const float *lat, const jano_grid *g, float *scores, void *stream) {
+  if (!lat || !scores) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a)) return JANO_E_INVAL;
+  return hip_status(jano::launch_fft_scores(lat, a, scores, static_cast<hipStream_t>(stream)));
+}
+
 int jano_levels(const float *scores, const jano_grid *g, int static_permille, int moderate_permille,
                 uint8_t *levels, int32_t *level_tok_counts, void *stream) {
   if (!scores || !levels || !level_tok_counts) return JANO_E_INVAL;

@@ -31,6 +31,8 @@ size_t analyze_ws_bytes(const AnalyzeGeom &g);
 // jano_analyze_scores: kernels 1 and 2 (scores [B]; ws holds the partials)
 hipError_t launch_analyze_scores(const float *lat, const AnalyzeGeom &g, float *scores, void *ws,
                                  hipStream_t s);
+// jano_fft_scores: the FFT complexity baseline's block scores [B]
+hipError_t launch_fft_scores(const float *lat, const AnalyzeGeom &g, float *scores, hipStream_t s);
 // jano_levels: kernels 3 and 4 (levels [B], tokens per level [3])
 hipError_t launch_levels(const float *scores, const AnalyzeGeom &g, int nS, int nSM, uint8_t *levels,
                          int32_t *counts, hipStream_t s);

@@ -19,7 +19,8 @@ JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_
 
 EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
-    "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_levels", "jano_analyze",
+    "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_fft_scores", "jano_levels",
+    "jano_analyze",
     "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
     "jano_writeback_step", "jano_qkv_proj",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
@@ -85,6 +86,7 @@ def lib():
             "jano_qkv_proj": ([vp, i64, i64, vp, i64, vp, i32, i32, gp, ctypes.c_float, vp, vp, vp, vp], i32),
             "jano_writeback_step": ([vp, vp, i64, vp, vp, i64, i64, ctypes.c_float, vp], i32),
             "jano_analyze_scores": ([vp, gp, vp, vp, ctypes.c_size_t, vp], i32),
+            "jano_fft_scores": ([vp, gp, vp, vp], i32),
             "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
             "jano_analyze": ([vp, gp, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
             "jano_schedule": ([vp, gp, sp, i32, vp, vp, vp], i32),
@@ -206,6 +208,20 @@ def analyze_scores(lat, spec: GridSpec, scores=None, workspace=None):
     g = spec.c()
     _check("jano_analyze_scores", lib().jano_analyze_scores(
         _ptr(lat), ctypes.byref(g), _ptr(scores), _ptr(workspace), workspace.numel(), _stream(lat)))
+    return scores
+
+
+def fft_scores(lat, spec: GridSpec, scores=None):
+    """jano_fft_scores. lat fp32 [K,C,F,H,W] on device -> the FFT complexity
+    baseline's block scores fp32 [B] on the device (an alternative index
+    source: rank them with levels() like the analyzer's scores)."""
+    torch = _torch()
+    _need(lat, "lat", torch.float32, (spec.K, spec.C, spec.F, spec.H, spec.W))
+    B, _ = grid_sizes(spec)
+    scores = torch.empty(B, dtype=torch.float32, device=lat.device) if scores is None else scores
+    _need(scores, "scores", torch.float32, (B,), lat.device)
+    g = spec.c()
+    _check("jano_fft_scores", lib().jano_fft_scores(_ptr(lat), ctypes.byref(g), _ptr(scores), _stream(lat)))
     return scores
 
 
