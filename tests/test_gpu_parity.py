@@ -211,6 +211,8 @@ def test_fft_scores_configs(torch, cfg, signal):
     ((3, 5, 2, 8, 2100), (1, 8, 1)),       # 2100 block columns: two column passes
     ((3, 1, 1, 4, 4), (1, 4, 4)),          # one block
     ((3, 2, 2, 9, 20), (1, 4, 8)),         # 16-byte loads, ragged last block column and row
+    ((3, 1, 3, 700, 2), (3, 700, 1)),      # 2100 rows per block, two blocks
+    ((3, 2, 3, 700, 8), (3, 700, 4)),      # the same with 16-byte loads and two channels
 ])
 def test_fft_scores_shapes(torch, shape, block):
     print("fft scores shape", shape, block, flush=True)
