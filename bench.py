@@ -465,8 +465,10 @@ def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
     t0 = time.perf_counter()
     O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
     t = time.perf_counter() - t0
-    if t < seconds_hint / 3:   # grow the sample to roughly the time hint
-        n_s = int(min(N, n_s * max(1.0, seconds_hint / max(t, 1e-3))))
+    # grow the sample until one pass takes about half the time hint or more
+    # (small samples run slower per query, so one extrapolation falls short)
+    while t < seconds_hint / 2 and n_s < N:
+        n_s = int(min(N, n_s * max(1.5, seconds_hint / max(t, 1e-3))))
         rows = np.sort(rng.choice(N, size=n_s, replace=False))
         t0 = time.perf_counter()
         O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
