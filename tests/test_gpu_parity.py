@@ -516,6 +516,25 @@ def test_attention_ragged(torch, n, N, d):
     assert_attn_close(host_bf16_f64(out), ref, "ragged n=%d N=%d d=%d" % (n, N, d))
 
 
+def test_empty_step_is_a_no_op(torch):
+    # a step with no due token: attention of zero queries and a scatter of
+    # zero rows write nothing and leave both caches as they were
+    rng = np.random.default_rng(3)
+    N, H = 300, 2
+    for d in (64, 128):
+        Kb = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+        Vb = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+        Kc, Vc = dev_bf16(Kb), dev_bf16(Vb)
+        empty = torch.empty((0, H, d), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty(0, dtype=torch.int32, device="cuda")
+        out = jano.attn_step(empty, empty, empty, idx, Kc, Vc)
+        out2 = jano.attention(empty, Kc, Vc)
+        torch.cuda.synchronize()
+        assert out.shape[0] == 0 and out2.shape[0] == 0
+        np.testing.assert_array_equal(host_bits(Kc), Kb)
+        np.testing.assert_array_equal(host_bits(Vc), Vb)
+
+
 def test_attention_peaked_and_scale(torch):
     # large logits exercise the running-max rescale; an explicit scale is used
     cfg = configs.IMAGE
