@@ -345,6 +345,29 @@ def attn_step(Q_act_bits, Knew_bits, Vnew_bits, idx, Kc_bits, Vc_bits, scale=Non
 # theirs, and every token takes the sampler step with that output.
 # --------------------------------------------------------------------------
 
+def f32_round_once(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """fp32 value nearest to the exact sum a + b (ties to even), for fp64
+    arrays a and b whose exact sum fits fp64's exponent range.
+
+    The fp64 sum s = fl(a + b) can itself be rounded, and rounding s again to
+    fp32 may then land on the other side of an fp32 midpoint. So the exact
+    error e = (a + b) - s is recovered with Knuth's TwoSum, and an inexact s
+    is moved to its odd neighbour on the side of the exact sum (rounding to
+    odd); rounding a round-to-odd value with p >= 24 + 2 bits to fp32 gives
+    the correctly rounded fp32 result (Boldo and Melquiond, "When double
+    rounding is odd", 2005)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    s = a + b
+    bv = s - a
+    e = (a - (s - bv)) + (b - bv)                 # exact: a + b = s + e
+    even = (s.view(np.int64) & 1) == 0
+    fix = (e != 0) & even
+    toward = np.where(e > 0, np.inf, -np.inf)
+    s = np.where(fix, np.nextafter(s, toward), s)
+    return s.astype(np.float32)
+
+
 def writeback_step(out_act_bits, idx, out_full_bits, x, dt):
     """Returns (out_full', x').
 
@@ -352,12 +375,13 @@ def writeback_step(out_act_bits, idx, out_full_bits, x, dt):
     tokens idx; out_full_bits [N, P] bf16 bits: every token's latest output;
     x [N, P] fp32 sampler state (token-major latent patches). The active rows
     of out_full are replaced, then x' = x + dt * out_full' elementwise (one
-    Euler step), evaluated exactly in fp64 (a bf16 x fp32 product is exact, and
-    the sum is correctly rounded) and rounded once to fp32."""
+    Euler step) rounded once to fp32: the bf16 x fp32 product has at most
+    8 + 24 significant bits and is exact in fp64, and the sum with x is
+    rounded to fp32 exactly once (f32_round_once)."""
     of = scatter_rows(out_full_bits, idx, out_act_bits)
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
-    x2 = x64 + np.float64(np.float32(dt)) * bf16_to_f64(of)
-    return of, x2.astype(np.float32)
+    prod = np.float64(np.float32(dt)) * bf16_to_f64(of)
+    return of, f32_round_once(x64, prod)
 
 
 # --------------------------------------------------------------------------

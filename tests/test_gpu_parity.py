@@ -348,6 +348,28 @@ def test_writeback_edges(torch):
     _wb_check(torch, x, full, act, idx, 0.0)
 
 
+def test_writeback_rounds_once(torch):
+    # x + dt*v = 1 + 2^-23 + 2^-24 - 2^-54 just below an fp32 midpoint: the
+    # correctly rounded step is 1 + 2^-23 (a sum formed in fp64 and then
+    # rounded to fp32 would give 1 + 2^-22). Placed in the 16-byte vector body
+    # and in the scalar tail, and through the unaligned path.
+    print("writeback rounds once", flush=True)
+    N, P = 37, 5
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal((N, P)).astype(np.float32)
+    full = synth.f32_to_bf16_bits(rng.standard_normal((N, P)).astype(np.float32))
+    for (n, p) in ((0, 0), (3, 2), (N - 1, P - 1)):
+        x[n, p] = np.float32(1.0 + 2.0 ** -23)
+        full[n, p] = 0x3F9A
+    act = full[[5, 9]].copy()
+    idx = np.array([5, 9], np.int32)
+    dt = np.float32(13944699 * 2.0 ** -48)
+    _, ref_x = O.writeback_step(act, idx, full, x, dt)
+    assert float(ref_x[0, 0]) == 1.0 + 2.0 ** -23 and float(ref_x[N - 1, P - 1]) == 1.0 + 2.0 ** -23
+    _wb_check(torch, x, full, act, idx, dt)
+    _wb_check(torch, x, full, act, idx, dt, x_off=1)
+
+
 # ------------------------------------------------------------------ schedule
 
 def test_schedule_all_steps_480p(torch):

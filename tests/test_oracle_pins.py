@@ -7,6 +7,8 @@ scale, a scatter that touches other rows) fails at least one of them.
 """
 import itertools
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -448,8 +450,58 @@ def test_writeback_dt_zero_and_empty():
     np.testing.assert_array_equal(of, full)
 
 
+def _rn32_exact(q: Fraction) -> np.float32:
+    """fp32 nearest to the rational q, ties to the even significand: the
+    candidates are the fp32 values around float(q), compared exactly."""
+    c = np.float32(float(q))
+    cands = {float(c), float(np.nextafter(c, np.float32(np.inf))),
+             float(np.nextafter(c, np.float32(-np.inf)))}
+    best = min(cands, key=lambda v: (abs(Fraction(v) - q),
+                                     int(np.array(v, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def _bf16_fraction(bits) -> Fraction:
+    return Fraction(float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0]))
+
+
+def test_writeback_rounds_once_counterexample():
+    # x + dt*v = 1 + 2^-23 + 2^-24 - 2^-54: just below the fp32 midpoint
+    # between 1 + 2^-23 and 1 + 2^-22, so the nearest fp32 is 1 + 2^-23. The
+    # nearest fp64 of that sum is the midpoint itself, and a second rounding
+    # of it to fp32 (ties to even) would give 1 + 2^-22.
+    x = np.array([[1.0 + 2.0 ** -23]], np.float32)
+    dt = np.float32(13944699 * 2.0 ** -48)
+    exact = Fraction(float(x[0, 0])) + Fraction(float(dt)) * _bf16_fraction(0x3F9A)
+    assert exact == 1 + Fraction(1, 2 ** 23) + Fraction(1, 2 ** 24) - Fraction(1, 2 ** 54)
+    _, x2 = O.writeback_step(np.array([[0x3F9A]], np.uint16), np.array([0]),
+                             np.zeros((1, 1), np.uint16), x, dt)
+    assert float(x2[0, 0]) == 1.0 + 2.0 ** -23
+    assert float(np.float32(float(exact))) == 1.0 + 2.0 ** -22   # the twice-rounded value
+
+
+def test_f32_round_once_against_exact_rationals():
+    # random sums and sums placed near fp32 midpoints, against the exact
+    # rational sum rounded to the nearest fp32 value
+    rng = np.random.default_rng(23)
+    a = rng.standard_normal(400).astype(np.float32).astype(np.float64)
+    b = (rng.standard_normal(400) * 2.0 ** rng.integers(-40, 2, 400)).astype(np.float32).astype(np.float64)
+    # b = half an fp32 ulp of a, plus or minus a few 2^-35 ulp: a + b lies
+    # within 2^-58 |a| of an fp32 midpoint, below fp64's own resolution there
+    ulp = np.spacing(np.abs(a).astype(np.float32)).astype(np.float64) * np.sign(a)
+    off = rng.integers(-3, 4, 400) * 2.0 ** -35
+    b = np.concatenate([b, ulp * (0.5 + off)])
+    a = np.concatenate([a, a])
+    naive = (a + b).astype(np.float32)        # fp64 sum, then fp32: twice rounded
+    assert (naive != O.f32_round_once(a, b)).sum() > 50
+    got = O.f32_round_once(a, b)
+    for i in range(a.size):
+        want = _rn32_exact(Fraction(float(a[i])) + Fraction(float(b[i])))
+        assert got[i].view(np.uint32) == want.view(np.uint32), i
+
+
 def test_writeback_bruteforce_all_active():
-    # every token active: scalar loops with Python floats (fp64) rounded once
+    # every token active: scalar loops over exact rationals, rounded once
     rng, x, full = _wb_inputs(N=4, P=3, seed=9)
     act = rng.integers(0x3000, 0x4400, size=(4, 3), dtype=np.uint16)
     perm = np.array([2, 0, 3, 1])
@@ -457,8 +509,7 @@ def test_writeback_bruteforce_all_active():
     of, x2 = O.writeback_step(act, perm, full, x, dt)
     for i in range(4):
         for p in range(3):
-            v = float(np.array([int(act[i, p]) << 16], np.uint32).view(np.float32)[0])
-            want = np.float32(float(x[perm[i], p]) + float(dt) * v)
+            want = _rn32_exact(Fraction(float(x[perm[i], p])) + Fraction(float(dt)) * _bf16_fraction(act[i, p]))
             assert of[perm[i], p] == act[i, p]
             assert x2[perm[i], p] == want, (i, p)
 
@@ -471,9 +522,12 @@ def test_writeback_two_steps_compose():
     of1, x1 = O.writeback_step(act, idx, full, x, 0.5)
     of2, x2 = O.writeback_step(act, idx, of1, x1, 0.5)
     np.testing.assert_array_equal(of2, of1)
-    step = np.float64(0.5) * O.bf16_to_f64(of1)
-    want = ((x.astype(np.float64) + step).astype(np.float32).astype(np.float64) + step).astype(np.float32)
-    np.testing.assert_array_equal(x2, want)
+    for n in range(x.shape[0]):
+        for p in range(x.shape[1]):
+            v = Fraction(1, 2) * _bf16_fraction(of1[n, p])
+            once = _rn32_exact(Fraction(float(x[n, p])) + v)
+            assert x1[n, p] == once
+            assert x2[n, p] == _rn32_exact(Fraction(float(once)) + v)
 
 
 # ------------------------------------------------------- concatenated layout
