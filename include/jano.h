@@ -40,8 +40,14 @@ enum {
   JANO_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim)     */
   JANO_E_RANGE = -3,       /* index list out of range / not ascending       */
   JANO_E_WORKSPACE = -4,   /* workspace missing or too small                */
-  JANO_E_HIP = -5          /* a HIP launch reported an error                */
+  JANO_E_HIP = -5,         /* a HIP launch reported an error                */
+  JANO_E_SCRATCH = -6      /* problem exceeds the built-in scratch buffer   */
 };
+
+/* Size of the fixed per-device scratch array jano_analyze_noalloc uses in
+ * place of a workspace (4 MiB: the partial sums of grids up to, e.g., 16
+ * channels x 16384 blocks with one strip per block row). */
+#define JANO_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Latent history and token geometry.
  *   K x [C, F, H, W]  warm-up latents (K >= 3), fp32
@@ -149,6 +155,28 @@ int jano_levels(const float *scores, const jano_grid *g, int static_permille,
 int jano_analyze(const float *lat, const jano_grid *g, int static_permille,
                  int moderate_permille, float *scores, uint8_t *levels,
                  int32_t *level_tok_counts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * jano_analyze_noalloc -- jano_analyze for callers that cannot allocate
+ * device memory or hand over a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ * Arguments, outputs and results as jano_analyze, without ws/ws_bytes: the
+ * partial sums live in a fixed array of JANO_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, held until the process ends. The call allocates
+ * nothing. The first call on a device looks the array's device address up
+ * (with that device current, so the stream must belong to the current
+ * device); later calls reuse it.
+ *   Returns JANO_E_SCRATCH, with nothing launched, when the grid needs more
+ *   than JANO_NOALLOC_SCRATCH_BYTES (jano_analyze_workspace_bytes(g) tells).
+ *   Every call on one GPU shares that GPU's array: calls that may overlap in
+ *   time on one GPU (different streams, or different threads enqueueing
+ *   without ordering) race and must be serialised by the caller. Stream order
+ *   is enough: calls enqueued on one stream never overlap. The array needs no
+ *   clearing between calls (every word read was written by the same call).
+ */
+int jano_analyze_noalloc(const float *lat, const jano_grid *g, int static_permille,
+                         int moderate_permille, float *scores, uint8_t *levels,
+                         int32_t *level_tok_counts, void *stream);
 
 /*
  * jano_schedule -- active index list of one denoising step.

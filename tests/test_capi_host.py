@@ -63,7 +63,7 @@ def test_version_and_status_strings():
     assert jano.abi_version() == 1
     L = jano.lib()
     assert L.jano_status_string(0) == b"ok"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         assert L.jano_status_string(code) not in (b"ok", b"unknown status")
 
 
@@ -119,6 +119,28 @@ def test_block_limit_accepted():
     B, N = ctypes.c_int64(), ctypes.c_int64()
     assert L.jano_grid_sizes(ctypes.byref(g), ctypes.byref(B), ctypes.byref(N)) == jano.JANO_OK
     assert B.value == 16384
+
+
+def test_analyze_noalloc_rejects_before_touching_the_gpu():
+    # every case below returns before the scratch lookup or any launch
+    L = jano.lib()
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    g = _grid()
+    assert L.jano_analyze_workspace_bytes(ctypes.byref(g)) <= jano.NOALLOC_SCRATCH_BYTES
+    assert L.jano_analyze_noalloc(null, ctypes.byref(g), 400, 300, fake, fake, fake, None) == -1
+    assert L.jano_analyze_noalloc(fake, ctypes.byref(g), 400, 300, fake, null, fake, None) == -1
+    assert L.jano_analyze_noalloc(fake, ctypes.byref(g), 700, 400, fake, fake, fake, None) == -1
+    assert L.jano_analyze_noalloc(fake, None, 400, 300, fake, fake, fake, None) == -1
+    bad = _grid(K=2)
+    assert L.jano_analyze_noalloc(fake, ctypes.byref(bad), 400, 300, fake, fake, fake, None) == -1
+    # 64 channels x 16384 blocks of fp64 partial sums = 8 MiB > the 4 MiB array
+    big = _grid(K=3, C=64, F=1, H=1024, W=1024, bF=1, bH=8, bW=8)
+    need = L.jano_analyze_workspace_bytes(ctypes.byref(big))
+    assert need > jano.NOALLOC_SCRATCH_BYTES
+    assert L.jano_analyze_noalloc(fake, ctypes.byref(big), 400, 300, fake, fake, fake,
+                                  None) == jano.JANO_E_SCRATCH
+    assert b"scratch" in L.jano_status_string(jano.JANO_E_SCRATCH)
 
 
 def test_analyze_argument_errors():

@@ -4,10 +4,20 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/jano.h"
 #include "kernels.hpp"
 
 using jano::AnalyzeGeom;
+
+// Scratch memory of jano_analyze_noalloc: the analyzer's partial sums live in
+// this fixed array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy, at its own address, until the process ends. In host
+// code the name `scratch` is only a host-side stand-in, never a device
+// address: kernels get the address hipGetSymbolAddress returns for the current
+// device (scratch_device_ptr).
+static __device__ __align__(256) unsigned char scratch[JANO_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -70,6 +80,29 @@ int schedule_impl(const uint8_t *levels, const jano_grid *g, const jano_sched *s
   return hip_status(jano::launch_schedule(levels, s, idx, n_dev, stream));
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_device_ptr(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +117,7 @@ const char *jano_status_string(int status) {
     case JANO_E_RANGE: return "index out of range or not strictly ascending";
     case JANO_E_WORKSPACE: return "workspace missing or too small";
     case JANO_E_HIP: return "HIP launch error";
+    case JANO_E_SCRATCH: return "problem larger than the built-in scratch buffer (JANO_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -150,6 +184,22 @@ int jano_analyze(const float *lat, const jano_grid *g, int static_permille, int 
   AnalyzeGeom a;
   if (!grid_ok(g, &a) || !mix_ok(static_permille, moderate_permille)) return JANO_E_INVAL;
   if (!ws || ws_bytes < jano::analyze_ws_bytes(a)) return JANO_E_WORKSPACE;
+  int nS, nSM;
+  split_ranks(a.B, static_permille, moderate_permille, &nS, &nSM);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (jano::launch_analyze_scores(lat, a, scores, ws, s) != hipSuccess) return JANO_E_HIP;
+  return hip_status(jano::launch_levels(scores, a, nS, nSM, levels, level_tok_counts, s));
+}
+
+int jano_analyze_noalloc(const float *lat, const jano_grid *g, int static_permille,
+                         int moderate_permille, float *scores, uint8_t *levels,
+                         int32_t *level_tok_counts, void *stream) {
+  if (!lat || !scores || !levels || !level_tok_counts) return JANO_E_INVAL;
+  AnalyzeGeom a;
+  if (!grid_ok(g, &a) || !mix_ok(static_permille, moderate_permille)) return JANO_E_INVAL;
+  if (jano::analyze_ws_bytes(a) > sizeof(scratch)) return JANO_E_SCRATCH;
+  void *ws = nullptr;
+  if (scratch_device_ptr(&ws) != hipSuccess) return JANO_E_HIP;
   int nS, nSM;
   split_ranks(a.B, static_permille, moderate_permille, &nS, &nSM);
   hipStream_t s = static_cast<hipStream_t>(stream);

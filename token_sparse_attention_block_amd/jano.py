@@ -16,11 +16,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libjano.so")
 
 JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_E_HIP = 0, -1, -2, -3, -4, -5
+JANO_E_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = (
     "jano_abi_version", "jano_status_string", "jano_grid_sizes", "jano_schedule_count",
     "jano_analyze_workspace_bytes", "jano_analyze_scores", "jano_fft_scores", "jano_levels",
-    "jano_analyze",
+    "jano_analyze", "jano_analyze_noalloc",
     "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
     "jano_writeback_step", "jano_qkv_proj",
     "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
@@ -89,6 +91,7 @@ def lib():
             "jano_fft_scores": ([vp, gp, vp, vp], i32),
             "jano_levels": ([vp, gp, i32, i32, vp, vp, vp], i32),
             "jano_analyze": ([vp, gp, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp], i32),
+            "jano_analyze_noalloc": ([vp, gp, i32, i32, vp, vp, vp, vp], i32),
             "jano_schedule": ([vp, gp, sp, i32, vp, vp, vp], i32),
             "jano_gather_rows": ([vp, i64, i64, vp, i64, vp, vp], i32),
             "jano_scatter_kv": ([vp, vp, vp, i64, vp, vp, i64, i64, vp], i32),
@@ -189,6 +192,26 @@ def analyze(lat, spec: GridSpec, static_permille=400, moderate_permille=300,
     _check("jano_analyze", lib().jano_analyze(
         _ptr(lat), ctypes.byref(g), int(static_permille), int(moderate_permille), _ptr(scores),
         _ptr(levels), _ptr(counts), _ptr(workspace), workspace.numel(), _stream(lat)))
+    return scores, levels, counts
+
+
+def analyze_noalloc(lat, spec: GridSpec, scores, levels, counts, static_permille=400,
+                    moderate_permille=300):
+    """jano_analyze_noalloc: jano_analyze into caller-given outputs (scores
+    fp32 [B], levels uint8 [B], counts int32 [3] on lat's device) with the
+    library's fixed scratch array as workspace. Nothing is allocated."""
+    torch = _torch()
+    _need(lat, "lat", torch.float32, (spec.K, spec.C, spec.F, spec.H, spec.W))
+    B, _ = grid_sizes(spec)
+    dev = lat.device
+    _need(scores, "scores", torch.float32, (B,), dev)
+    _need(levels, "levels", torch.uint8, (B,), dev)
+    _need(counts, "counts", torch.int32, (3,), dev)
+    g = spec.c()
+    with torch.cuda.device(dev):
+        _check("jano_analyze_noalloc", lib().jano_analyze_noalloc(
+            _ptr(lat), ctypes.byref(g), int(static_permille), int(moderate_permille), _ptr(scores),
+            _ptr(levels), _ptr(counts), _stream(lat)))
     return scores, levels, counts
 
 
