@@ -144,6 +144,71 @@ def ingest_counters(fetch_path, write_path, workload, out_path=None):
     return out
 
 
+def summarize_trace(trace_csv, bench_log, out_md, command):
+    """Markdown summary of a rocprofv3 kernel trace (--output-format csv) taken
+    over a bench.py run, next to the bench line that run printed: per kernel
+    and grid the dispatch count and durations, and the headline attention
+    launch's average without its first (cold) dispatch set against the line's
+    roofline.achieved."""
+    import csv
+    rows = list(csv.DictReader(open(trace_csv)))
+    line = None
+    for l in open(bench_log):
+        l = l.strip()
+        if l.startswith("{") and '"metric"' in l:
+            line = json.loads(l)
+    if line is None:
+        raise SystemExit("no bench line in %s" % bench_log)
+
+    def grid(r):
+        gx = r.get("Grid_Size_X", r.get("Grid_Size", "0"))
+        return "%s,%s" % (gx, r.get("Grid_Size_Y", "1"))
+
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3    # us
+        key = (name, grid(r), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
+        groups.setdefault(key, []).append((int(r["Start_Timestamp"]), dur))
+    table = []
+    for (name, g, wg), v in groups.items():
+        v.sort()
+        d = [x[1] for x in v]
+        table.append((sum(d), name, g, wg, d))
+    table.sort(reverse=True)
+    cfg = line["config"]
+    flops = 4.0 * cfg["n_act"] * cfg["tokens"] * cfg["heads"] * cfg["head_dim"]
+    tile = line["roofline"].get("queries_per_workgroup", 384)
+    want_grid = "%d,%d" % (-(-cfg["n_act"] // tile) * 512, cfg["heads"])
+    att = [t for t in table if t[1].startswith("void attn_fwd_d128_kernel") or "attn_fwd_d128_kernel" in t[1]]
+    att = [t for t in att if t[2] == want_grid]
+    out = ["# Kernel trace of the bench run, %s" % cfg["workload"], "",
+           "Command (repository root, one MI355X, `export TMPDIR=/tmp` first):", "", "```", command, "```", "",
+           "Bench line printed by the same run (excerpt): value %.2f TFLOP/s, ms_per_step %.4f, "
+           "roofline.achieved %.2f TFLOP/s, frac %.5f." % (line["value"], line["ms_per_step"],
+                                                           line["roofline"]["achieved"], line["roofline"]["frac"]),
+           "", "Durations in microseconds (end - start per dispatch).", "",
+           "| kernel | grid (threads) x,y | block | calls | avg us | avg us w/o first | min us | max us | total ms |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for tot, name, g, wg, d in table[:24]:
+        nm = name if len(name) <= 90 else name[:87] + "..."
+        rest = d[1:] if len(d) > 1 else d
+        out.append("| `%s` | %s | %s | %d | %.2f | %.2f | %.2f | %.2f | %.3f |" % (
+            nm, g, wg, len(d), sum(d) / len(d), sum(rest) / len(rest), min(d), max(d), tot / 1e3))
+    if att:
+        d = att[0][4][1:] if len(att[0][4]) > 1 else att[0][4]
+        avg_ms = sum(d) / len(d) / 1e3
+        tf = flops / (avg_ms * 1e-3) / 1e12
+        out += ["", "Headline attention launch (grid %s): %d dispatches after the first, average %.3f ms, "
+                    "max %.3f ms -> %.4g FLOP / %.3f ms = %.1f TFLOP/s = %.4f of 2.5 PFLOP/s; the bench line's "
+                    "roofline.frac is %.4f (ratio %.4f). The run's ms_per_step is %.4f ms." % (
+                        att[0][2], len(d), avg_ms, max(d) / 1e3, flops, avg_ms, tf, tf / 2500.0,
+                        line["roofline"]["frac"], (tf / 2500.0) / line["roofline"]["frac"], line["ms_per_step"])]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def load_traffic(key, workload, path=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary, only
     if it was taken on the current kernel source; else None."""
@@ -216,16 +281,30 @@ def make_qkv(torch, synth, cfg):
 
 
 STEP_CALLS = ("analyze_scores", "levels", "schedule", "gather", "scatter", "attention")
+LAYERS = 3      # per-layer buffers the timed steps rotate through
 
 
-def run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, ev=None):
-    """One whole pass; `ev` (len(STEP_CALLS) + 1 events) brackets each call."""
+def make_layers(torch, jano, Q, K, V, n_layers=LAYERS):
+    """Per-layer device buffers, as a DiT holds one set per transformer layer:
+    the hidden rows the queries are gathered from and the full-sequence K/V
+    cache. Consecutive steps use consecutive layers, so the gather and the
+    scatter stream from HBM: the buffers they touch total several GB, far
+    above the 256 MB last-level cache."""
+    layers = []
+    for l in range(n_layers):
+        layers.append({"Q": Q.clone() if l else Q, "Kc": K.clone(), "Vc": V.clone()})
+    return layers
+
+
+def run_step(p, i, lay, ev=None):
+    """One whole pass on layer buffers `lay`; `ev` (len(STEP_CALLS) + 1
+    events) brackets each call."""
     jano = p.jano
     idx = p.idx[:p.n_act]
     calls = (lambda: p.analyze_scores(i), p.levels_, p.schedule,
-             lambda: jano.gather_rows(Q, idx, p.n_act, out=q_act),
-             lambda: jano.scatter_kv(Kn, Vn, idx, Kc, Vc, n_act=p.n_act),
-             lambda: jano.attention(q_act, Kc, Vc, out=out, n_q=p.n_act))
+             lambda: jano.gather_rows(lay["Q"], idx, p.n_act, out=lay["q_act"]),
+             lambda: jano.scatter_kv(lay["Kn"], lay["Vn"], idx, lay["Kc"], lay["Vc"], n_act=p.n_act),
+             lambda: jano.attention(lay["q_act"], lay["Kc"], lay["Vc"], out=lay["out"], n_q=p.n_act))
     if ev:
         ev[0].record()
     for j, call in enumerate(calls):
@@ -234,27 +313,34 @@ def run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, ev=None):
             ev[j + 1].record()
 
 
-def time_fraction(torch, jano, synth, cfg, frac, Q, K, V, Kc, Vc, steps, warmup):
+def time_fraction(torch, jano, synth, cfg, frac, K, V, layers, steps, warmup):
     p = Path(torch, jano, synth, cfg, frac)
     n = p.n_act
     H, d = cfg.heads, cfg.d
     idx = p.idx[:n]
     p.schedule()
-    Kn = jano.gather_rows(K, idx, n)     # fresh rows, as a projection would emit them
-    Vn = jano.gather_rows(V, idx, n)
-    q_act = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    for lay in layers:
+        # fresh rows of each layer, as its projection would emit them
+        lay["Kn"] = jano.gather_rows(K, idx, n)
+        lay["Vn"] = jano.gather_rows(V, idx, n)
+        lay["q_act"] = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+        lay["out"] = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    L = len(layers)
     for i in range(warmup):
-        run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out)
+        run_step(p, i, layers[i % L])
     torch.cuda.synchronize()
     evs = [[_ev(torch) for _ in range(len(STEP_CALLS) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(p, i, Q, Kn, Vn, Kc, Vc, q_act, out, evs[i])
+        run_step(p, i, layers[i % L], evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     per = {k: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, k in enumerate(STEP_CALLS)}
     per["analyze"] = per["analyze_scores"] + per["levels"]
+    per["attention_mean"] = float(np.mean([e[-2].elapsed_time(e[-1]) for e in evs]))
+    for lay in layers:
+        for k in ("Kn", "Vn", "q_act", "out"):
+            lay.pop(k)
     return p, n, wall * 1e3, per
 
 
@@ -368,17 +454,19 @@ def time_qkv_proj(torch, jano, cfg, idx, reps=5):
             "flops": flops, "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 5)}
 
 
-def time_dense(torch, jano, Q, Kc, Vc, reps):
+def time_dense(torch, jano, Q, Kc, Vc, reps=20):
+    """Median over `reps` launches of dense attention (every token a query),
+    each launch between its own pair of events."""
     out = torch.empty_like(Q)
     jano.attention(Q, Kc, Vc, out=out)
     torch.cuda.synchronize()
-    a, b = _ev(torch), _ev(torch)
-    a.record()
-    for _ in range(reps):
+    ev = [(_ev(torch), _ev(torch)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
         jano.attention(Q, Kc, Vc, out=out)
-    b.record()
+        b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
 def sched_run(torch, jano, synth, cfg):
@@ -439,41 +527,82 @@ def sched_run(torch, jano, synth, cfg):
     torch.cuda.synchronize()
     graph_total = a.elapsed_time(b)
     del g
-    dense = time_dense(torch, jano, Q, Kc, Vc, 3)
+    dense = time_dense(torch, jano, Q, Kc, Vc, 20)
     return {"workload": "480p-32760tok-12h-d128-50steps", "n_act_per_step": n_per,
+            "dense_ms_median_of_20": round(dense, 4),
+            "dense_TFLOP/s": round(4.0 * N * N * H * d / (dense * 1e-3) / 1e12, 2),
+            "queries_per_workgroup": {"dense": jano.attention_plan(N, H, d),
+                                      "interleaved": sorted({jano.attention_plan(n, H, d) for n in n_per})},
             "total_ms": round(total, 3), "graph_total_ms": round(graph_total, 3),
             "dense_50_steps_ms": round(50 * dense, 3),
             "speedup": round(50 * dense / total, 4), "graph_speedup": round(50 * dense / graph_total, 4),
             "ideal_attention_speedup": round(50 * N / sum(n_per), 4)}
 
 
-def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    attention of a sample of active queries (all heads) against the full
-    75.6k-token cache, fp64 NumPy."""
-    from oracle import jano_oracle as O
+def _host_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(cfg, synth, Qb, Kb, Vb, spm, mpm, step_id, seconds_hint=15.0):
+    """The oracle, as it stands, timed on this host's cores beside the GPU.
+
+    Every step of the path but attention runs in full at the workload's size
+    (the analyzer over all warm-up latents, levels, the step's index list, the
+    gather of the active query rows and the scatter of their fresh K/V rows).
+    Attention runs on a sample of active queries (all heads) against the full
+    K/V cache; its time for all active queries is extrapolated linearly and
+    labelled as such. `value` is the oracle's attention TFLOP/s on the sample."""
+    from oracle import jano_oracle as O
+    threads = _host_threads()
     N, H, d = cfg.N, cfg.heads, cfg.d
+    legs = {}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        legs[name] = round((time.perf_counter() - t0) * 1e3, 2)
+        return r
+
+    lat = synth.latents(cfg)
+    scores = timed("analyze_scores", lambda: O.analyze_scores(lat, cfg.block))
+    del lat
+    fhw = (cfg.F, cfg.H, cfg.W)
+    def levels_and_counts():
+        lv = O.assign_levels(scores, spm, mpm)
+        return lv, O.level_token_counts(lv, fhw, cfg.patch, cfg.block)
+    lv, _ = timed("levels", levels_and_counts)
+    sc = cfg.schedule
+    idx = timed("schedule", lambda: O.schedule(O.token_levels(lv, fhw, cfg.patch, cfg.block), step_id,
+                                               sc.T, sc.W, sc.Cd, sc.periods))
+    n_act = len(idx)
+    timed("gather", lambda: O.gather_rows(Qb, idx))
+    Kn, Vn = Kb[idx], Vb[idx]
+    timed("scatter", lambda: (O.scatter_rows(Kb, idx, Kn), O.scatter_rows(Vb, idx, Vn)))
+    del Kn, Vn
+
     n_s = 64
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(N, size=n_s, replace=False))
+    rows = np.sort(rng.choice(n_act, size=n_s, replace=False))
     Kf, Vf = O.bf16_to_f64(Kb), O.bf16_to_f64(Vb)
     t0 = time.perf_counter()
-    O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
+    O.attention(O.bf16_to_f64(Qb[idx[rows]]), Kf, Vf)
     t = time.perf_counter() - t0
     # grow the sample until one pass takes about half the time hint or more
     # (small samples run slower per query, so one extrapolation falls short)
-    while t < seconds_hint / 2 and n_s < N:
-        n_s = int(min(N, n_s * max(1.5, seconds_hint / max(t, 1e-3))))
-        rows = np.sort(rng.choice(N, size=n_s, replace=False))
+    while t < seconds_hint / 2 and n_s < n_act:
+        n_s = int(min(n_act, n_s * max(1.5, seconds_hint / max(t, 1e-3))))
+        rows = np.sort(rng.choice(n_act, size=n_s, replace=False))
         t0 = time.perf_counter()
-        O.attention(O.bf16_to_f64(Qb[rows]), Kf, Vf)
+        O.attention(O.bf16_to_f64(Qb[idx[rows]]), Kf, Vf)
         t = time.perf_counter() - t0
+    del Kf, Vf
     flops = 4.0 * n_s * N * H * d
+    attn_ms = t * 1e3 * n_act / n_s
+    step_ms = sum(legs[k] for k in ("analyze_scores", "levels", "schedule", "gather", "scatter")) + attn_ms
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -486,8 +615,12 @@ def cpu_baseline(cfg, Qb, Kb, Vb, seconds_hint=15.0):
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(t, 2), "cpu_model": model,
             "host_cpus": os.cpu_count(),
-            "sample": "%d active queries x %d heads against the full %d-token K/V cache "
-                      "(fp64 NumPy attention; analyzer/schedule/gather/scatter excluded)" % (n_s, H, N)}
+            "sample": "attention: %d of the step's %d active queries x %d heads against the full "
+                      "%d-token K/V cache (fp64 NumPy); analyzer, levels, schedule, gather and "
+                      "scatter in full at the same size" % (n_s, n_act, H, N),
+            "oracle_ms": legs,
+            "oracle_attention_ms_extrapolated": round(attn_ms, 1),
+            "oracle_step_ms_extrapolated": round(step_ms, 1)}
 
 
 def measure_ceilings(torch, reps=10):
@@ -581,9 +714,14 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline fraction only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("TRACE_CSV", "BENCH_LOG", "OUT_MD", "COMMAND"),
+                    help="write a markdown summary of a rocprofv3 kernel trace of a bench run and exit")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH", "WRITE"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc outputs (CSV or .db) and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        summarize_trace(*args.trace_summary)
+        return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, "720p-active%d" % round(100 * args.frac))
         return
@@ -614,17 +752,17 @@ def main():
     Q, K, V = (upload_bf16(torch, b) for b in (Qb, Kb, Vb))
     if args.no_cpu:
         del Qb, Kb, Vb
-    Kc, Vc = K.clone(), V.clone()
+    layers = make_layers(torch, jano, Q, K, V)
 
     print("bench: headline fraction %.2f" % args.frac, file=sys.stderr, flush=True)
-    p, n_act, ms_step, per = time_fraction(torch, jano, synth, cfg, args.frac, Q, K, V, Kc, Vc,
+    p, n_act, ms_step, per = time_fraction(torch, jano, synth, cfg, args.frac, K, V, layers,
                                            args.steps, args.warmup)
     small = time_small_calls(torch, p)
     per.update(small)
     per["analyze"] = per["analyze_scores"] + per["levels"]
     attn_flops = 4.0 * n_act * N * H * d
     value = attn_flops / (ms_step * 1e-3) / 1e12
-    achieved = attn_flops / (per["attention"] * 1e-3) / 1e12
+    achieved = attn_flops / (per["attention_mean"] * 1e-3) / 1e12   # average launch
     lat_bytes = cfg.latent_bytes + p.B * 4      # latents read, scores written
     fft_bytes = cfg.latent_bytes // cfg.K + p.B * 4   # the latest latent read, scores written
     row_bytes = H * d * 2
@@ -668,7 +806,7 @@ def main():
     writeback = time_writeback(torch, jano, cfg, p.idx[:n_act])
 
     print("bench: dense reference", file=sys.stderr, flush=True)
-    dense_ms = time_dense(torch, jano, Q, Kc, Vc, 3)
+    dense_ms = time_dense(torch, jano, Q, layers[0]["Kc"], layers[0]["Vc"], 20)
     dense_tflops = 4.0 * N * N * H * d / (dense_ms * 1e-3) / 1e12
     speedups = {}
     path_ms_head = per["gather"] + per["scatter"] + per["attention"]
@@ -681,13 +819,13 @@ def main():
             if abs(f - args.frac) < 1e-9:
                 continue
             print("bench: fraction %.2f" % f, file=sys.stderr, flush=True)
-            pf, nf, _, perf = time_fraction(torch, jano, synth, cfg, f, Q, K, V, Kc, Vc, 3, 1)
+            pf, nf, _, perf = time_fraction(torch, jano, synth, cfg, f, K, V, layers, 6, 3)
             pm = perf["gather"] + perf["scatter"] + perf["attention"]
             speedups["%d%%" % round(100 * f)] = {
                 "n_act": nf, "path_ms": round(pm, 4), "speedup": round(dense_ms / pm, 4),
                 "attention_TFLOP/s": round(4.0 * nf * N * H * d / (perf["attention"] * 1e-3) / 1e12, 2)}
             del pf
-        del Q, K, V, Kc, Vc
+        del Q, K, V, layers
         torch.cuda.empty_cache()
         print("bench: 50-step interleaved run (480p)", file=sys.stderr, flush=True)
         extra["sched480p"] = sched_run(torch, jano, synth, configs.SCHED480)
@@ -703,7 +841,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("bench: CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, Qb, Kb, Vb)
+        cpu = cpu_baseline(cfg, synth, Qb, Kb, Vb, p.spm, p.mpm, p.step_id)
 
     line = {
         "metric": "active-query attention TFLOP/s + step speedup vs dense at 75.6k tokens",
@@ -725,7 +863,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": load_traffic("attention", wl),
-                     "kernel": "attn_fwd_d128_kernel"},
+                     "kernel": "attn_fwd_d128_kernel",
+                     "queries_per_workgroup": jano.attention_plan(n_act, H, d),
+                     "launch_ms_median": round(per["attention"], 4),
+                     "launch_ms_mean": round(per["attention_mean"], 4)},
         "cpu_baseline": cpu,
         "step_speedup_vs_dense": speedups,
         "dense": {"ms": round(dense_ms, 4), "TFLOP/s": round(dense_tflops, 3)},

@@ -277,6 +277,16 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
 
 /*
+ * jano_attention_plan -- host helper (no device access): the number of
+ * queries per workgroup (query tile) jano_attention and jano_attn_step use
+ * for n_q queries of H heads at head dim d. d = 128 takes 384-query tiles, or
+ * 256-query tiles when those finish the launch in fewer rounds of the GPU's
+ * compute units (one workgroup per unit at a time); d = 64 takes 128.
+ * Errors: JANO_E_INVAL (n_q or H below 1, null output), JANO_E_UNSUPPORTED (d).
+ */
+int jano_attention_plan(int64_t n_q, int H, int d, int32_t *queries_per_workgroup);
+
+/*
  * jano_attn_step -- one interleaved-step attention: jano_scatter_kv of the
  * fresh rows into the cache, then jano_attention of the active queries against
  * the whole cache, on one stream (the scatter completes before attention reads).

@@ -251,3 +251,19 @@ def test_binding_rejects_cpu_tensors():
         jano.attention(x, x, x)
     with pytest.raises(ValueError):
         jano.analyze(torch.zeros(5, 16, 1, 16, 16), jano.GridSpec.of(configs.TINY))
+
+
+def test_attention_plan_tiles():
+    # 384-query tiles unless 256-query tiles finish in fewer rounds of 256 CUs
+    assert jano.attention_plan(75600, 40, 128) == 384      # 7880 vs 11840 workgroups
+    assert jano.attention_plan(18468, 40, 128) == 384
+    assert jano.attention_plan(32760, 12, 128) == 256      # 1032 (5 rounds) vs 1536 (6 x 0.72)
+    assert jano.attention_plan(200, 3, 128) == 256         # one round either way
+    assert jano.attention_plan(300, 256, 128) == 384       # one round against two
+    assert jano.attention_plan(10, 1, 64) == 128
+    L = jano.lib()
+    q = ctypes.c_int32()
+    assert L.jano_attention_plan(0, 1, 128, ctypes.byref(q)) == jano.JANO_E_INVAL
+    assert L.jano_attention_plan(10, 0, 128, ctypes.byref(q)) == jano.JANO_E_INVAL
+    assert L.jano_attention_plan(10, 1, 96, ctypes.byref(q)) == jano.JANO_E_UNSUPPORTED
+    assert L.jano_attention_plan(10, 1, 128, None) == jano.JANO_E_INVAL

@@ -448,8 +448,21 @@ def test_check_idx(torch):
 
 # ----------------------------------------------------------------- attention
 
+_QKV_MEMO = {}
+
+
+def _qkv(cfg, extra=0):
+    """synth.qkv_bits, kept for the next test of the same workload (drawing
+    the 720p tensors takes longer than the parity check itself)."""
+    key = (cfg.name, extra)
+    if key not in _QKV_MEMO:
+        _QKV_MEMO.clear()
+        _QKV_MEMO[key] = synth.qkv_bits(cfg, extra=extra)
+    return _QKV_MEMO[key]
+
+
 def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0):
-    Qb, Kb, Vb = synth.qkv_bits(cfg, extra=extra)
+    Qb, Kb, Vb = _qkv(cfg, extra)
     if q_mult != 1.0:
         Qb = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(Qb) * np.float32(q_mult))
     rng = np.random.default_rng(11 + extra)
@@ -469,6 +482,16 @@ def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0):
     return got[rows], ref
 
 
+# rows checked at full size: the first and last query (first and last
+# workgroup tile, ragged tail) and 512 seeded others, every head of each
+SAMPLE_ROWS = 512
+
+
+def _sample_rows(n, seed=17):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, SAMPLE_ROWS), replace=False)]))
+
+
 @pytest.mark.parametrize("cfg,frac", [(configs.TINY, 0.3), (configs.IMAGE, 0.3), (configs.IMAGE, 1.0)],
                          ids=["tiny-30", "image-30", "image-100"])
 def test_attention_full_compare(torch, cfg, frac):
@@ -478,16 +501,31 @@ def test_attention_full_compare(torch, cfg, frac):
     assert_attn_close(got, ref, "%s %.0f%%" % (cfg.name, 100 * frac))
 
 
-@pytest.mark.parametrize("cfg,frac", [(configs.V480, 0.25), (configs.V720, 0.25), (configs.V720, 0.10)],
-                         ids=["480p-25", "720p-25", "720p-10"])
+@pytest.mark.parametrize("cfg,frac", [(configs.V480, 0.25), (configs.V720, 0.10), (configs.V720, 0.25),
+                                      (configs.V720, 0.50)],
+                         ids=["480p-25", "720p-10", "720p-25", "720p-50"])
 def test_attention_full_size_sampled(torch, cfg, frac):
+    # the interleaved steps the bench times (scatter + active-query attention)
     print("attention sampled", cfg.name, frac, flush=True)
     idx = _idx_for(cfg, frac)
-    rng = np.random.default_rng(17)
-    n = len(idx)
-    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, 192), replace=False)]))
+    sample = _sample_rows(len(idx))
     got, ref = _attn_case(torch, cfg, idx, sample=sample)
     assert_attn_close(got, ref, "%s %.0f%% sampled" % (cfg.name, 100 * frac))
+
+
+@pytest.mark.parametrize("cfg", [configs.V480, configs.V720], ids=["480p-dense", "720p-dense"])
+def test_dense_full_size_sampled(torch, cfg):
+    # the dense reference step (every token a query), the denominator of the
+    # step speedups and of the 50-step run's total
+    print("attention dense sampled", cfg.name, flush=True)
+    Qb, Kb, Vb = _qkv(cfg)
+    out = jano.attention(dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb))
+    torch.cuda.synchronize()
+    rows = _sample_rows(cfg.N, seed=19)
+    got = host_bf16_f64(out)[rows]
+    del out
+    ref = O.attention(O.bf16_to_f64(Qb[rows]), O.bf16_to_f64(Kb), O.bf16_to_f64(Vb))
+    assert_attn_close(got, ref, "%s dense sampled" % cfg.name)
 
 
 def test_full_activation_equals_dense(torch):
@@ -522,13 +560,20 @@ def test_cached_equals_recompute(torch):
 # d = 128 cases cover a cache shorter than one 64-key tile (1, 63), whole
 # tiles only (64, 128), one extra key (65, 129, 4097) and a mid-tile tail
 # (1000); query counts straddle the 384-query workgroup tile.
-@pytest.mark.parametrize("n,N,d", [(1, 1, 64), (31, 100, 64), (129, 65, 128), (200, 1000, 128),
-                                   (64, 129, 64), (257, 4097, 128), (5, 1, 128), (48, 63, 128),
-                                   (100, 64, 128), (384, 128, 128), (385, 129, 128)])
-def test_attention_ragged(torch, n, N, d):
-    print("attention ragged", n, N, d, flush=True)
+# d = 128 runs in 256-query tiles for launches that fit one round of the GPU
+# (H = 3 here) and in 384-query tiles when those take fewer rounds (the H = 256
+# cases: one round of 384-query tiles against two of 256); each form gets
+# ragged query and key tails.
+@pytest.mark.parametrize("n,N,d,H,tile", [
+    (1, 1, 64, 3, 128), (31, 100, 64, 3, 128), (64, 129, 64, 3, 128),
+    (129, 65, 128, 3, 256), (200, 1000, 128, 3, 256), (257, 4097, 128, 3, 256),
+    (5, 1, 128, 3, 256), (48, 63, 128, 3, 256), (100, 64, 128, 3, 256), (384, 128, 128, 3, 256),
+    (385, 129, 128, 3, 256), (300, 1000, 128, 256, 384), (384, 128, 128, 256, 384),
+    (257, 65, 128, 256, 384), (300, 1, 128, 256, 384)])
+def test_attention_ragged(torch, n, N, d, H, tile):
+    print("attention ragged", n, N, d, H, flush=True)
+    assert jano.attention_plan(n, H, d) == tile
     rng = np.random.default_rng(n * 7 + N)
-    H = 3
     Q = synth.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
     K = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
     V = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
@@ -574,8 +619,8 @@ def test_attention_peaked_and_scale(torch):
 
 
 @pytest.mark.parametrize("case", ["mid-tile", "ragged-tail", "double"])
-@pytest.mark.parametrize("d", [128, 64])
-def test_attention_late_max_jumps(torch, d, case):
+@pytest.mark.parametrize("d,H,tile", [(128, 2, 256), (128, 256, 384), (64, 2, 128)])
+def test_attention_late_max_jumps(torch, d, H, tile, case):
     """The running max jumps past the rescale slack (2^8) after many tiles,
     with N = 1000 = 15 tiles of 64 + a ragged tile of 40. Every query shares
     a component of 4 that meets chosen keys with a large value; the other
@@ -587,7 +632,8 @@ def test_attention_late_max_jumps(torch, d, case):
     softmax weight, so a wrong rescale of what was accumulated before it
     shows in the output."""
     rng = np.random.default_rng(31 + d)
-    n, N, H = 100, 1000, 2
+    n, N = (300 if H > 2 else 100), 1000
+    assert jano.attention_plan(n, H, d) == tile
     c = 1.4426950408889634 / np.sqrt(d)          # log2 units per unit of q . k
     Q = 0.1 * rng.standard_normal((n, H, d)).astype(np.float32)
     K = 0.1 * rng.standard_normal((N, H, d)).astype(np.float32)
@@ -606,7 +652,7 @@ def test_attention_late_max_jumps(torch, d, case):
     out = jano.attention(dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb))
     torch.cuda.synchronize()
     ref = O.attention(O.bf16_to_f64(Qb), O.bf16_to_f64(Kb), O.bf16_to_f64(Vb))
-    assert_attn_close(host_bf16_f64(out), ref, "late max jump %s d=%d" % (case, d))
+    assert_attn_close(host_bf16_f64(out), ref, "late max jump %s d=%d H=%d" % (case, d, H))
 
 
 def test_attention_closed_forms(torch):

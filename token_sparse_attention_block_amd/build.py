@@ -1,6 +1,10 @@
 """Builds libjano.so (HIP for gfx950) in-tree with hipcc, and beside it
 libjano_calib.so, the calibration kernel that measurements use to find the
-matrix-core rate the part sustains (not part of the Jano path).
+matrix-core rate the part sustains (not part of the Jano path), and
+libjano_asan.so, the same library with its host code (argument checks,
+launch set-up) built with AddressSanitizer for host-only ABI tests. The
+device code of the ASan build is compiled as usual; only the host pass is
+instrumented.
 
     python -m token_sparse_attention_block_amd.build [-v]
 
@@ -23,6 +27,10 @@ LIB = os.path.join(LIBDIR, "libjano.so")
 SOURCES = ["capi.hip", "analyze.hip", "schedule.hip", "rows.hip", "attention.hip", "proj.hip"]
 CALIB_LIB = os.path.join(LIBDIR, "libjano_calib.so")
 CALIB_SOURCES = ["calib/mfma_loop.hip"]
+ASAN_LIB = os.path.join(LIBDIR, "libjano_asan.so")
+ASAN_OBJ = os.path.join(OBJ, "asan")
+# host pass only: each sanitizer flag goes to the host compiler alone
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -57,24 +65,44 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, asan: bool = True) -> str:
     cc = hipcc()
     os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(ASAN_OBJ, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    libs = ((LIB, SOURCES), (CALIB_LIB, CALIB_SOURCES))
+    # (library, sources, object dir, extra compile flags, extra link flags)
+    libs = [(LIB, SOURCES, OBJ, [], []), (CALIB_LIB, CALIB_SOURCES, OBJ, [], [])]
+    if asan:
+        libs.append((ASAN_LIB, SOURCES, ASAN_OBJ, ["-g"] + ASAN_HOST,
+                     ["-Xarch_host", "-fsanitize=address", "-shared-libsan"]))
+
+    def obj(d, s):
+        return os.path.join(d, s.replace("/", "_").replace(".hip", ".o"))
+
     cmds = []
-    for _, sources in libs:
+    for _, sources, d, cflags, _ in libs:
         for s in sources:
-            o = os.path.join(OBJ, s.replace("/", "_").replace(".hip", ".o"))
-            cmds.append([cc] + COMMON + EXTRA.get(s, []) + ["-c", os.path.join(SRC, s), "-o", o])
+            cmds.append([cc] + COMMON + EXTRA.get(s, []) + cflags + ["-c", os.path.join(SRC, s), "-o", obj(d, s)])
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    for lib, sources in libs:
-        objs = [os.path.join(OBJ, s.replace("/", "_").replace(".hip", ".o")) for s in sources]
+    for lib, sources, d, _, lflags in libs:
         tmp = lib + ".tmp"
-        _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + lflags + ["-o", tmp] +
+             [obj(d, s) for s in sources], verbose)
         os.replace(tmp, lib)
     return LIB
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime that libjano_asan.so needs preloaded (the
+    Python interpreter itself is not instrumented)."""
+    cc = os.path.realpath(hipcc())
+    out = subprocess.run([os.path.join(os.path.dirname(os.path.dirname(cc)), "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if out.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("ASan runtime not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -278,8 +278,6 @@ constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
 //   when it extends past N, goes through the clamped per-row path. That tile
 //   is also the only one whose scores are masked (keys >= N get -inf).
 // ---------------------------------------------------------------------------
-constexpr int kQW2 = 48;                    // queries per wave
-constexpr int kBM2 = kW2 * kQW2;           // 384 queries per workgroup
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz_v2(int r) { return 2 * (r & 7); }
@@ -311,11 +309,16 @@ __device__ __forceinline__ void issue_tile_full(const char *kbase, const char *v
   }
 }
 
+// G query groups of 16 per wave: G = 3 (384 queries per workgroup) is the
+// fast form; G = 2 (256 per workgroup) loses some LDS reuse but fills the
+// last round of a launch whose 384-query tiles would leave most CUs idle.
+template <int G>
 __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2) {
   constexpr int D = 128;
-  constexpr int G = 3;                      // query groups of 16
+  constexpr int kQW2 = 16 * G;              // queries per wave
+  constexpr int kBM2 = kW2 * kQW2;          // queries per workgroup
   __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
 
   const int tid = threadIdx.x;
@@ -429,16 +432,16 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
         for (int g = 0; g < G; ++g)
           s[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[g][t], s[g][b], 0, 0, 0);
       }
-    // schedule: 4 K reads ahead, then one read per 3 MFMAs, so each read has
-    // 12 MFMAs (~190 cycles) to land; left to itself the compiler waits on
-    // each read right after issuing it
+    // schedule: 4 K reads ahead, then one read per G MFMAs, so each read has
+    // 4G MFMAs (~190 cycles at G = 3) to land; left to itself the compiler
+    // waits on each read right after issuing it
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // 4 LDS reads
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // 3 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, G, 0);  // G MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);   // last 12 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G, 0);  // last 4G MFMAs
 
     bf16x8 pb[G][kBN / 32];
 #pragma unroll
@@ -521,20 +524,46 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   }
 }
 
+// Query groups per wave of the d = 128 kernel for one launch. Each CU holds one
+// workgroup (128 KB of LDS), so a launch runs in ceil(workgroups / CUs)
+// rounds of equal length; the form with the fewest rounds x round cost wins.
+// A G = 2 round costs about kCostG2 of a G = 3 round (two thirds of the work
+// at a lower LDS reuse per fragment).
+constexpr int kCUs = 256;
+constexpr float kCostG2 = 0.72f;
+
+int attn_groups_d128(int64_t nq, int H) {
+  const int64_t wg3 = (nq + 383) / 384 * H, wg2 = (nq + 255) / 256 * H;
+  const float t3 = static_cast<float>((wg3 + kCUs - 1) / kCUs);
+  const float t2 = static_cast<float>((wg2 + kCUs - 1) / kCUs) * kCostG2;
+  return t2 < t3 ? 2 : 3;
+}
+
 }  // namespace
+
+int attention_tile_queries(int64_t nq, int H, int d) {
+  return d == 128 ? kW2 * 16 * attn_groups_d128(nq, H) : kBM;
+}
 
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, const uint16_t *V,
                             int64_t N, int H, int d, float scale, uint16_t *out, hipStream_t s) {
   if (nq == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>((nq + kBM - 1) / kBM), static_cast<unsigned>(H));
   if (d == 128) {
-    const dim3 grid3(static_cast<unsigned>((nq + kBM2 - 1) / kBM2), static_cast<unsigned>(H));
-    hipLaunchKernelGGL(attn_fwd_d128_kernel, grid3, dim3(kW2 * kWave), 0, s, Q, K, V, out,
-                       static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
-  } else
+    const int G = attn_groups_d128(nq, H);
+    const int bm = kW2 * 16 * G;
+    const dim3 grid(static_cast<unsigned>((nq + bm - 1) / bm), static_cast<unsigned>(H));
+    if (G == 2)
+      hipLaunchKernelGGL(attn_fwd_d128_kernel<2>, grid, dim3(kW2 * kWave), 0, s, Q, K, V, out,
+                         static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
+    else
+      hipLaunchKernelGGL(attn_fwd_d128_kernel<3>, grid, dim3(kW2 * kWave), 0, s, Q, K, V, out,
+                         static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
+  } else {
+    const dim3 grid(static_cast<unsigned>((nq + kBM - 1) / kBM), static_cast<unsigned>(H));
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, Q, K, V, out,
                        static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
+  }
   return hipGetLastError();
 }
 

@@ -264,6 +264,13 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
                                            static_cast<hipStream_t>(stream)));
 }
 
+int jano_attention_plan(int64_t n_q, int H, int d, int32_t *queries_per_workgroup) {
+  if (!queries_per_workgroup || n_q < 1 || H < 1 || n_q > kMaxRows) return JANO_E_INVAL;
+  if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
+  *queries_per_workgroup = jano::attention_tile_queries(n_q, H, d);
+  return JANO_OK;
+}
+
 int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
                    const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
                    int d, float scale, uint16_t *out, void *stream) {

@@ -13,7 +13,9 @@ import os
 from dataclasses import dataclass
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libjano.so")
+# JANO_LIB selects another build of the same library (the host-ASan build in
+# the host-only ABI tests); the default is the in-tree libjano.so
+LIB_PATH = os.environ.get("JANO_LIB") or os.path.join(PKG, "lib", "libjano.so")
 
 JANO_OK, JANO_E_INVAL, JANO_E_UNSUPPORTED, JANO_E_RANGE, JANO_E_WORKSPACE, JANO_E_HIP = 0, -1, -2, -3, -4, -5
 JANO_E_SCRATCH = -6
@@ -25,7 +27,7 @@ EXPORTS = (
     "jano_analyze", "jano_analyze_noalloc",
     "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
     "jano_writeback_step", "jano_qkv_proj",
-    "jano_scatter_kv", "jano_attention", "jano_attn_step", "jano_check_idx",
+    "jano_scatter_kv", "jano_attention", "jano_attention_plan", "jano_attn_step", "jano_check_idx",
 )
 
 
@@ -96,6 +98,7 @@ def lib():
             "jano_gather_rows": ([vp, i64, i64, vp, i64, vp, vp], i32),
             "jano_scatter_kv": ([vp, vp, vp, i64, vp, vp, i64, i64, vp], i32),
             "jano_attention": ([vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
+            "jano_attention_plan": ([i64, i32, i32, ctypes.POINTER(ctypes.c_int32)], i32),
             "jano_attn_step": ([vp, vp, vp, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
             "jano_check_idx": ([vp, i64, i64, vp, vp], i32),
         }
@@ -158,6 +161,13 @@ def grid_sizes(spec: GridSpec):
 def analyze_workspace_bytes(spec: GridSpec) -> int:
     g = spec.c()
     return lib().jano_analyze_workspace_bytes(ctypes.byref(g))
+
+
+def attention_plan(n_q, H, d) -> int:
+    """jano_attention_plan: queries per workgroup of the attention launch."""
+    q = ctypes.c_int32()
+    _check("jano_attention_plan", lib().jano_attention_plan(int(n_q), int(H), int(d), ctypes.byref(q)))
+    return q.value
 
 
 def schedule_count(level_tok_counts, T, W, Cd, periods, step) -> int:
