@@ -319,6 +319,11 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   constexpr int D = 128;
   constexpr int kQW2 = 16 * G;              // queries per wave
   constexpr int kBM2 = kW2 * kQW2;          // queries per workgroup
+  // LDS fragment reads issued ahead of the MFMAs that use them: the 2-group
+  // form has the registers to hold 8 K and 8 V^T fragments in flight (+2% on
+  // the 480p shapes against 4 and none); at 3 groups the register file is full
+  constexpr int kSAhead = G == 2 ? 8 : 4;
+  constexpr int kPVAhead = G == 2 ? 8 : 0;
   __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
 
   const int tid = threadIdx.x;
@@ -432,16 +437,16 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
         for (int g = 0; g < G; ++g)
           s[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[g][t], s[g][b], 0, 0, 0);
       }
-    // schedule: 4 K reads ahead, then one read per G MFMAs, so each read has
-    // 4G MFMAs (~190 cycles at G = 3) to land; left to itself the compiler
-    // waits on each read right after issuing it
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // 4 LDS reads
+    // schedule: kSAhead K reads ahead, then one read per G MFMAs, so each
+    // read has kSAhead * G MFMAs to land (~190 cycles at G = 3); left to
+    // itself the compiler waits on each read right after issuing it
+    __builtin_amdgcn_sched_group_barrier(0x100, kSAhead, 0);    // reads ahead
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 16 - kSAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, G, 0);  // G MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * G, 0);  // last 4G MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, kSAhead * G, 0);  // last MFMAs
 
     bf16x8 pb[G][kBN / 32];
 #pragma unroll
@@ -504,6 +509,16 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
         for (int g = 0; g < G; ++g)
           o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[g][ks], o[g][db], 0, 0, 0);
       }
+    if constexpr (kPVAhead > 0) {
+      // the same for the V^T fragments (two transposing reads each)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPVAhead, 1);
+#pragma unroll
+      for (int i = 0; i < 16 - kPVAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, G, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPVAhead * G, 1);
+    }
   };
   for (int j = 0; j < nfull; ++j) tile(j, std::false_type{});
   if (nfull < ntiles) tile(nfull, std::true_type{});
