@@ -449,9 +449,24 @@ def time_qkv_proj(torch, jano, cfg, idx, reps=5):
     ms = a.elapsed_time(b) / reps
     flops = 2.0 * n * Dm * 3 * H * d
     tf = flops / (ms * 1e-3) / 1e12
-    del X, W, out
+    # the vendor GEMM on the same product shape, rows pre-gathered and no
+    # rotation (the same FLOPs, less work): a ceiling for this shape
+    Xa = X[idx.long()].contiguous()
+    Wt = W.t().contiguous()
+    C = torch.empty((n, 3 * H * d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        torch.matmul(Xa, Wt, out=C)
+    a.record()
+    for _ in range(reps):
+        torch.matmul(Xa, Wt, out=C)
+    b.record()
+    torch.cuda.synchronize()
+    vtf = flops / (a.elapsed_time(b) / reps * 1e-3) / 1e12
+    del X, W, out, Xa, Wt, C
     return {"ms": round(ms, 4), "n_act": n, "hidden": Dm, "out_features": 3 * H * d,
-            "flops": flops, "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 5)}
+            "flops": flops, "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 5),
+            "vendor_gemm_same_shape_TFLOP/s": round(vtf, 2),
+            "frac_of_vendor_same_shape": round(tf / vtf, 4)}
 
 
 def time_dense(torch, jano, Q, Kc, Vc, reps=20):
