@@ -1,5 +1,7 @@
 """Host logic of the bench (CPU only): the HBM-traffic ingestion from
-rocprofv3 counter output and the source-hash gate on its use."""
+rocprofv3 counter output and the source-hash gate on its use, the
+kernel-trace summary set against the bench line, and the CPU baseline's
+oracle legs on a small workload."""
 import json
 import sqlite3
 
@@ -60,3 +62,47 @@ def test_traffic_used_only_for_the_profiled_source(tmp_path):
     assert bench.load_traffic("gather", "wl", path=out) is None      # source changed since
     assert bench.load_traffic("scatter", "wl", path=out) is None     # never profiled
     assert bench.load_traffic("attention", "other", path=out) is None
+
+
+def test_trace_summary_sets_the_profile_against_the_line(tmp_path):
+    # a kernel trace whose headline attention launches take 20, 10, 10 ms
+    # (the first is the cold one) and a bench line with frac for 10 ms
+    import csv
+    trace = tmp_path / "t.csv"
+    n_act, N, H, d = 18468, 75600, 40, 128
+    grid = -(-n_act // 384) * 512
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+                    "Workgroup_Size_X"])
+        t = 0
+        for dur in (20e6, 10e6, 10e6):
+            w.writerow(["void jano::(anonymous namespace)::attn_fwd_d128_kernel<3>(x)", t, t + int(dur),
+                        grid, H, 512])
+            t += int(dur) + 1000
+        w.writerow(["gather_rows_v16(x)", t, t + 60000, 11819520, 1, 640])
+    flops = 4.0 * n_act * N * H * d
+    achieved = flops / 10e-3 / 1e12
+    line = {"metric": "m", "value": 1.0, "ms_per_step": 10.5, "config": {"workload": "w", "n_act": n_act,
+            "tokens": N, "heads": H, "head_dim": d},
+            "roofline": {"achieved": achieved, "frac": achieved / 2500.0, "queries_per_workgroup": 384}}
+    log = tmp_path / "b.log"
+    log.write_text("bench: noise\n" + json.dumps(line) + "\n")
+    out = tmp_path / "s.md"
+    bench.summarize_trace(str(trace), str(log), str(out), "rocprofv3 ... -- python bench.py")
+    text = out.read_text()
+    assert "2 dispatches after the first, average 10.000 ms" in text
+    assert "(ratio 1.0000)" in text
+    assert "| 3 | 13333.33 | 10000.00 |" in text          # calls, mean, mean without the first
+
+
+def test_cpu_baseline_runs_every_leg_on_a_small_workload():
+    from token_sparse_attention_block_amd import configs, synth
+    cfg = configs.TINY
+    Qb, Kb, Vb = synth.qkv_bits(cfg)
+    sc = cfg.schedule
+    got = bench.cpu_baseline(cfg, synth, Qb, Kb, Vb, 450, 300, sc.W + 1, seconds_hint=0.2)
+    assert got["kind"] == "oracle" and got["unit"] == "TFLOP/s" and got["value"] > 0
+    assert set(got["oracle_ms"]) == {"analyze_scores", "levels", "schedule", "gather", "scatter"}
+    assert got["oracle_step_ms_extrapolated"] >= got["oracle_attention_ms_extrapolated"]
+    assert got["cores"] >= 1
