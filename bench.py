@@ -178,8 +178,8 @@ def summarize_trace(trace_csv, bench_log, out_md, command):
     table.sort(reverse=True)
     cfg = line["config"]
     flops = 4.0 * cfg["n_act"] * cfg["tokens"] * cfg["heads"] * cfg["head_dim"]
-    tile = line["roofline"].get("queries_per_workgroup", 384)
-    want_grid = "%d,%d" % (-(-cfg["n_act"] // tile) * 512, cfg["heads"])
+    k3, m2 = line["roofline"]["tiles_per_head_384_256"]
+    want_grid = "%d,1" % ((k3 + m2) * cfg["heads"] * 512)      # one workgroup of 512 per tile
     att = [t for t in table if t[1].startswith("void attn_fwd_d128_kernel") or "attn_fwd_d128_kernel" in t[1]]
     att = [t for t in att if t[2] == want_grid]
     out = ["# Kernel trace of the bench run, %s" % cfg["workload"], "",
@@ -546,8 +546,8 @@ def sched_run(torch, jano, synth, cfg):
     return {"workload": "480p-32760tok-12h-d128-50steps", "n_act_per_step": n_per,
             "dense_ms_median_of_20": round(dense, 4),
             "dense_TFLOP/s": round(4.0 * N * N * H * d / (dense * 1e-3) / 1e12, 2),
-            "queries_per_workgroup": {"dense": jano.attention_plan(N, H, d),
-                                      "interleaved": sorted({jano.attention_plan(n, H, d) for n in n_per})},
+            "tiles_per_head_384_256": {"dense": list(jano.attention_plan(N, H, d)[:2]),
+                                       "interleaved": sorted({tuple(jano.attention_plan(n, H, d)[:2]) for n in n_per})},
             "total_ms": round(total, 3), "graph_total_ms": round(graph_total, 3),
             "dense_50_steps_ms": round(50 * dense, 3),
             "speedup": round(50 * dense / total, 4), "graph_speedup": round(50 * dense / graph_total, 4),
@@ -879,7 +879,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 5),
                      "traffic": load_traffic("attention", wl),
                      "kernel": "attn_fwd_d128_kernel",
-                     "queries_per_workgroup": jano.attention_plan(n_act, H, d),
+                     "tiles_per_head_384_256": list(jano.attention_plan(n_act, H, d)[:2]),
                      "launch_ms_median": round(per["attention"], 4),
                      "launch_ms_mean": round(per["attention_mean"], 4)},
         "cpu_baseline": cpu,

@@ -277,14 +277,18 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
 
 /*
- * jano_attention_plan -- host helper (no device access): the number of
- * queries per workgroup (query tile) jano_attention and jano_attn_step use
- * for n_q queries of H heads at head dim d. d = 128 takes 384-query tiles, or
- * 256-query tiles when those finish the launch in fewer rounds of the GPU's
- * compute units (one workgroup per unit at a time); d = 64 takes 128.
+ * jano_attention_plan -- host helper (no device access): how jano_attention
+ * and jano_attn_step split the n_q queries of each of H heads into
+ * workgroup tiles at head dim d.
+ *   tiles_per_head (out) [3]: [0] tiles of 384 queries, [1] tiles of 256
+ *   queries (d = 128), [2] tiles of 128 queries (d = 64). With d = 128 a head
+ *   is covered by [0] tiles from its first query on, then [1] tiles (the
+ *   last tile of the head may be ragged); the 256-query workgroups run last,
+ *   to fill the launch's final round on the GPU's compute units (one
+ *   workgroup per unit at a time).
  * Errors: JANO_E_INVAL (n_q or H below 1, null output), JANO_E_UNSUPPORTED (d).
  */
-int jano_attention_plan(int64_t n_q, int H, int d, int32_t *queries_per_workgroup);
+int jano_attention_plan(int64_t n_q, int H, int d, int32_t *tiles_per_head);
 
 /*
  * jano_attn_step -- one interleaved-step attention: jano_scatter_kv of the

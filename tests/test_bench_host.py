@@ -70,22 +70,22 @@ def test_trace_summary_sets_the_profile_against_the_line(tmp_path):
     import csv
     trace = tmp_path / "t.csv"
     n_act, N, H, d = 18468, 75600, 40, 128
-    grid = -(-n_act // 384) * 512
+    grid = (44 + 7) * H * 512
     with open(trace, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
                     "Workgroup_Size_X"])
         t = 0
         for dur in (20e6, 10e6, 10e6):
-            w.writerow(["void jano::(anonymous namespace)::attn_fwd_d128_kernel<3>(x)", t, t + int(dur),
-                        grid, H, 512])
+            w.writerow(["jano::(anonymous namespace)::attn_fwd_d128_kernel(x)", t, t + int(dur),
+                        grid, 1, 512])
             t += int(dur) + 1000
         w.writerow(["gather_rows_v16(x)", t, t + 60000, 11819520, 1, 640])
     flops = 4.0 * n_act * N * H * d
     achieved = flops / 10e-3 / 1e12
     line = {"metric": "m", "value": 1.0, "ms_per_step": 10.5, "config": {"workload": "w", "n_act": n_act,
             "tokens": N, "heads": H, "head_dim": d},
-            "roofline": {"achieved": achieved, "frac": achieved / 2500.0, "queries_per_workgroup": 384}}
+            "roofline": {"achieved": achieved, "frac": achieved / 2500.0, "tiles_per_head_384_256": [44, 7]}}
     log = tmp_path / "b.log"
     log.write_text("bench: noise\n" + json.dumps(line) + "\n")
     out = tmp_path / "s.md"

@@ -254,16 +254,24 @@ def test_binding_rejects_cpu_tensors():
 
 
 def test_attention_plan_tiles():
-    # 384-query tiles unless 256-query tiles finish in fewer rounds of 256 CUs
-    assert jano.attention_plan(75600, 40, 128) == 384      # 7880 vs 11840 workgroups
-    assert jano.attention_plan(18468, 40, 128) == 384
-    assert jano.attention_plan(32760, 12, 128) == 256      # 1032 (5 rounds) vs 1536 (6 x 0.72)
-    assert jano.attention_plan(200, 3, 128) == 256         # one round either way
-    assert jano.attention_plan(300, 256, 128) == 384       # one round against two
-    assert jano.attention_plan(10, 1, 64) == 128
+    # per head: (384-query tiles, 256-query tiles, 128-query tiles)
+    assert jano.attention_plan(75600, 40, 128) == (197, 0, 0)     # 30.8 rounds: all 384
+    assert jano.attention_plan(18468, 40, 128) == (44, 7, 0)      # 7.66 rounds -> 44 full + 7 of 256
+    assert jano.attention_plan(37848, 40, 128) == (96, 4, 0)
+    assert jano.attention_plan(32760, 12, 128) == (0, 128, 0)     # 4.03 rounds of 384 -> 6 of 256
+    assert jano.attention_plan(200, 3, 128) == (0, 1, 0)          # one round either way
+    assert jano.attention_plan(300, 256, 128) == (1, 0, 0)        # one round against two
+    assert jano.attention_plan(10, 1, 64) == (0, 0, 1)
+    for n, H in ((18468, 40), (37848, 40), (19640, 12), (1151, 128), (1299, 96), (7, 1)):
+        k3, m2, _ = jano.attention_plan(n, H, 128)
+        if k3 and m2:
+            # mixed: full 384-query tiles, then 256-query tiles covering the rest
+            assert 384 * k3 < n <= 384 * k3 + 256 * m2 < n + 256
+        else:
+            assert 384 * k3 + 256 * m2 >= n
     L = jano.lib()
-    q = ctypes.c_int32()
-    assert L.jano_attention_plan(0, 1, 128, ctypes.byref(q)) == jano.JANO_E_INVAL
-    assert L.jano_attention_plan(10, 0, 128, ctypes.byref(q)) == jano.JANO_E_INVAL
-    assert L.jano_attention_plan(10, 1, 96, ctypes.byref(q)) == jano.JANO_E_UNSUPPORTED
+    t = (ctypes.c_int32 * 3)()
+    assert L.jano_attention_plan(0, 1, 128, t) == jano.JANO_E_INVAL
+    assert L.jano_attention_plan(10, 0, 128, t) == jano.JANO_E_INVAL
+    assert L.jano_attention_plan(10, 1, 96, t) == jano.JANO_E_UNSUPPORTED
     assert L.jano_attention_plan(10, 1, 128, None) == jano.JANO_E_INVAL

@@ -560,19 +560,21 @@ def test_cached_equals_recompute(torch):
 # d = 128 cases cover a cache shorter than one 64-key tile (1, 63), whole
 # tiles only (64, 128), one extra key (65, 129, 4097) and a mid-tile tail
 # (1000); query counts straddle the 384-query workgroup tile.
-# d = 128 runs in 256-query tiles for launches that fit one round of the GPU
-# (H = 3 here) and in 384-query tiles when those take fewer rounds (the H = 256
-# cases: one round of 384-query tiles against two of 256); each form gets
-# ragged query and key tails.
-@pytest.mark.parametrize("n,N,d,H,tile", [
-    (1, 1, 64, 3, 128), (31, 100, 64, 3, 128), (64, 129, 64, 3, 128),
-    (129, 65, 128, 3, 256), (200, 1000, 128, 3, 256), (257, 4097, 128, 3, 256),
-    (5, 1, 128, 3, 256), (48, 63, 128, 3, 256), (100, 64, 128, 3, 256), (384, 128, 128, 3, 256),
-    (385, 129, 128, 3, 256), (300, 1000, 128, 256, 384), (384, 128, 128, 256, 384),
-    (257, 65, 128, 256, 384), (300, 1, 128, 256, 384)])
-def test_attention_ragged(torch, n, N, d, H, tile):
+# d = 128 launches cover each head with 384-query tiles, 256-query tiles, or
+# full 384-query tiles followed by 256-query ones (jano_attention_plan); the
+# cases below run each form with ragged query and key tails: 256 only for
+# launches that fit one round of the GPU (H = 3), 384 only where those take
+# fewer rounds (H = 256), and the mixed form (H = 96 and 128).
+@pytest.mark.parametrize("n,N,d,H,tiles", [
+    (1, 1, 64, 3, (0, 0, 1)), (31, 100, 64, 3, (0, 0, 1)), (64, 129, 64, 3, (0, 0, 1)),
+    (129, 65, 128, 3, (0, 1, 0)), (200, 1000, 128, 3, (0, 1, 0)), (257, 4097, 128, 3, (0, 2, 0)),
+    (5, 1, 128, 3, (0, 1, 0)), (48, 63, 128, 3, (0, 1, 0)), (100, 64, 128, 3, (0, 1, 0)),
+    (384, 128, 128, 3, (0, 2, 0)), (385, 129, 128, 3, (0, 2, 0)), (300, 1000, 128, 256, (1, 0, 0)),
+    (384, 128, 128, 256, (1, 0, 0)), (257, 65, 128, 256, (1, 0, 0)), (300, 1, 128, 256, (1, 0, 0)),
+    (1151, 300, 128, 128, (2, 2, 0)), (1299, 1000, 128, 96, (2, 3, 0)), (1151, 64, 128, 128, (2, 2, 0))])
+def test_attention_ragged(torch, n, N, d, H, tiles):
     print("attention ragged", n, N, d, H, flush=True)
-    assert jano.attention_plan(n, H, d) == tile
+    assert jano.attention_plan(n, H, d) == tiles
     rng = np.random.default_rng(n * 7 + N)
     Q = synth.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
     K = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
@@ -619,8 +621,9 @@ def test_attention_peaked_and_scale(torch):
 
 
 @pytest.mark.parametrize("case", ["mid-tile", "ragged-tail", "double"])
-@pytest.mark.parametrize("d,H,tile", [(128, 2, 256), (128, 256, 384), (64, 2, 128)])
-def test_attention_late_max_jumps(torch, d, H, tile, case):
+@pytest.mark.parametrize("d,H,n,tiles", [(128, 2, 100, (0, 1, 0)), (128, 256, 300, (1, 0, 0)),
+                                         (128, 128, 1151, (2, 2, 0)), (64, 2, 100, (0, 0, 1))])
+def test_attention_late_max_jumps(torch, d, H, n, tiles, case):
     """The running max jumps past the rescale slack (2^8) after many tiles,
     with N = 1000 = 15 tiles of 64 + a ragged tile of 40. Every query shares
     a component of 4 that meets chosen keys with a large value; the other
@@ -632,8 +635,8 @@ def test_attention_late_max_jumps(torch, d, H, tile, case):
     softmax weight, so a wrong rescale of what was accumulated before it
     shows in the output."""
     rng = np.random.default_rng(31 + d)
-    n, N = (300 if H > 2 else 100), 1000
-    assert jano.attention_plan(n, H, d) == tile
+    N = 1000
+    assert jano.attention_plan(n, H, d) == tiles
     c = 1.4426950408889634 / np.sqrt(d)          # log2 units per unit of q . k
     Q = 0.1 * rng.standard_normal((n, H, d)).astype(np.float32)
     K = 0.1 * rng.standard_normal((N, H, d)).astype(np.float32)

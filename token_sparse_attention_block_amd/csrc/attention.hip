@@ -313,28 +313,21 @@ __device__ __forceinline__ void issue_tile_full(const char *kbase, const char *v
 // fast form; G = 2 (256 per workgroup) loses some LDS reuse but fills the
 // last round of a launch whose 384-query tiles would leave most CUs idle.
 template <int G>
-__global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
+__device__ __forceinline__ void attn_tile_d128(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2) {
+    uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2, int head, int q0,
+    char (*lds)[2][kTileB]) {
   constexpr int D = 128;
   constexpr int kQW2 = 16 * G;              // queries per wave
-  constexpr int kBM2 = kW2 * kQW2;          // queries per workgroup
   // LDS fragment reads issued ahead of the MFMAs that use them: the 2-group
   // form has the registers to hold 8 K and 8 V^T fragments in flight (+2% on
   // the 480p shapes against 4 and none); at 3 groups the register file is full
   constexpr int kSAhead = G == 2 ? 8 : 4;
   constexpr int kPVAhead = G == 2 ? 8 : 0;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int l16 = lane & 15, h4 = lane >> 4;
-  const int nwg = gridDim.x * gridDim.y;
-  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
-  const int xcd = lin % kXcdsAttn, xslot = lin / kXcdsAttn;
-  const int logical = xcd * (nwg / kXcdsAttn) + min(xcd, nwg % kXcdsAttn) + xslot;
-  const int qtile = logical % gridDim.x;
-  const int head = logical / gridDim.x;
   const size_t rs = static_cast<size_t>(H) * D;
   const uint16_t *Kh = K + static_cast<size_t>(head) * D;
   const uint16_t *Vh = V + static_cast<size_t>(head) * D;
@@ -367,7 +360,7 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   bf16x8 qf[G][D / 32];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    qrow[g] = qtile * kBM2 + wave * kQW2 + 16 * g + l16;
+    qrow[g] = q0 + wave * kQW2 + 16 * g + l16;
     const uint16_t *qp = Q + static_cast<size_t>(min(qrow[g], nq - 1)) * rs +
                          static_cast<size_t>(head) * D + 8 * h4;
 #pragma unroll
@@ -539,25 +532,107 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   }
 }
 
-// Query groups per wave of the d = 128 kernel for one launch. Each CU holds one
-// workgroup (128 KB of LDS), so a launch runs in ceil(workgroups / CUs)
-// rounds of equal length; the form with the fewest rounds x round cost wins.
-// A G = 2 round costs about kCostG2 of a G = 3 round (two thirds of the work
-// at a lower LDS reuse per fragment).
-constexpr int kCUs = 256;
-constexpr float kCostG2 = 0.72f;
+// Workgroup i of a phase of n workgroups, renumbered so that the workgroups
+// one XCD (one L2) receives -- the hardware deals them out round-robin --
+// are consecutive: an XCD works through whole heads in turn.
+__device__ __forceinline__ int xcd_order(int i, int n) {
+  const int x = i % kXcdsAttn;
+  return x * (n / kXcdsAttn) + min(x, n % kXcdsAttn) + i / kXcdsAttn;
+}
 
-int attn_groups_d128(int64_t nq, int H) {
-  const int64_t wg3 = (nq + 383) / 384 * H, wg2 = (nq + 255) / 256 * H;
-  const float t3 = static_cast<float>((wg3 + kCUs - 1) / kCUs);
-  const float t2 = static_cast<float>((wg2 + kCUs - 1) / kCUs) * kCostG2;
-  return t2 < t3 ? 2 : 3;
+// One launch of the d = 128 kernel: each head's queries are covered by k3
+// tiles of 384 (workgroups 0 .. H*k3-1) and then m2 tiles of 256 (the rest,
+// dispatched last), so a launch's last round can be filled with shorter
+// workgroups. Both phases are numbered XCD by XCD (xcd_order). FORM 3 and
+// FORM 2 are the launches with only one tile size (m2 = 0, or k3 = 0),
+// compiled without the other form's code; FORM 0 holds both.
+template <int FORM>
+__global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2, int k3, int m2) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
+  const int i = blockIdx.x, n3 = H * k3;
+  if (FORM == 3 || (FORM == 0 && i < n3)) {
+    const int t = xcd_order(i, n3);
+    attn_tile_d128<3>(Q, K, V, out, nq, N, H, scale_log2, t / k3, 384 * (t % k3), lds);
+  } else {
+    const int t = xcd_order(i - n3, H * m2);
+    attn_tile_d128<2>(Q, K, V, out, nq, N, H, scale_log2, t / m2, 384 * k3 + 256 * (t % m2), lds);
+  }
+}
+
+// Tiles of the d = 128 kernel for one launch. One workgroup fills a CU
+// (128 KB of LDS), every workgroup streams all N keys, so a 384-query
+// workgroup takes one unit of time and a 256-query one kCostG2 units
+// (measured 0.69-0.71: two thirds of the matrix and softmax work at the same
+// LDS reads per tile). Each XCD runs its share of the 384-query workgroups
+// and then of the 256-query ones on its 32 CUs, taking the next workgroup
+// whenever a CU frees; the plan with the earliest modelled finish wins
+// among all-384 (ragged last tile), all-256, and k3 full 384-query tiles per
+// head followed by 256-query tiles for the rest.
+constexpr int kCUs = 256;
+constexpr int kCUsPerXcd = kCUs / kXcdsAttn;
+constexpr double kCostG2 = 0.70;
+
+double xcd_finish(int64_t n3, int64_t n2) {
+  const int64_t P = kCUsPerXcd, r = n3 / P, q = n3 % P;
+  const double t3 = static_cast<double>(r + (q ? 1 : 0));
+  if (n2 == 0) return t3;
+  // 256-query workgroups go to the CU that frees first: P - q CUs from time
+  // r, q CUs from time r + 1
+  double last = 0.0;
+  int64_t a = 0, b = 0, left = n2;
+  while (left > 0) {
+    const double te = r + a * kCostG2;
+    const double tl = q ? r + 1 + b * kCostG2 : 1e300;
+    if (te <= tl) {
+      left -= P - q;
+      last = te;
+      ++a;
+    } else {
+      left -= q;
+      last = tl;
+      ++b;
+    }
+  }
+  return last + kCostG2 > t3 ? last + kCostG2 : t3;
+}
+
+double plan_finish(int64_t k3, int64_t m2, int H) {
+  const int64_t n3 = k3 * H, n2 = m2 * H;
+  return xcd_finish((n3 + kXcdsAttn - 1) / kXcdsAttn, (n2 + kXcdsAttn - 1) / kXcdsAttn);
+}
+
+void plan_d128(int64_t nq, int H, int *k3, int *m2) {
+  int64_t bk = (nq + 383) / 384, bm = 0;                    // all 384, ragged last tile
+  double best = plan_finish(bk, 0, H);
+  auto consider = [&](int64_t k, int64_t m) {
+    const double f = plan_finish(k, m, H);
+    if (f < best - 1e-9) {
+      best = f;
+      bk = k;
+      bm = m;
+    }
+  };
+  consider(0, (nq + 255) / 256);                            // all 256
+  const int64_t kfull = nq / 384;
+  for (int64_t k = kfull; k >= 1 && k >= kfull - 32; --k) consider(k, (nq - 384 * k + 255) / 256);
+  *k3 = static_cast<int>(bk);
+  *m2 = static_cast<int>(bm);
 }
 
 }  // namespace
 
-int attention_tile_queries(int64_t nq, int H, int d) {
-  return d == 128 ? kW2 * 16 * attn_groups_d128(nq, H) : kBM;
+void attention_tiles(int64_t nq, int H, int d, int32_t tiles[3]) {
+  tiles[0] = tiles[1] = tiles[2] = 0;
+  if (d == 128) {
+    int k3, m2;
+    plan_d128(nq, H, &k3, &m2);
+    tiles[0] = k3;
+    tiles[1] = m2;
+  } else {
+    tiles[2] = static_cast<int32_t>((nq + kBM - 1) / kBM);
+  }
 }
 
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, const uint16_t *V,
@@ -565,15 +640,12 @@ hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, co
   if (nq == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
   if (d == 128) {
-    const int G = attn_groups_d128(nq, H);
-    const int bm = kW2 * 16 * G;
-    const dim3 grid(static_cast<unsigned>((nq + bm - 1) / bm), static_cast<unsigned>(H));
-    if (G == 2)
-      hipLaunchKernelGGL(attn_fwd_d128_kernel<2>, grid, dim3(kW2 * kWave), 0, s, Q, K, V, out,
-                         static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
-    else
-      hipLaunchKernelGGL(attn_fwd_d128_kernel<3>, grid, dim3(kW2 * kWave), 0, s, Q, K, V, out,
-                         static_cast<int>(nq), static_cast<int>(N), H, scale_log2);
+    int k3, m2;
+    plan_d128(nq, H, &k3, &m2);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(H) * (k3 + m2)));
+    auto kernel = m2 == 0 ? attn_fwd_d128_kernel<3> : k3 == 0 ? attn_fwd_d128_kernel<2> : attn_fwd_d128_kernel<0>;
+    hipLaunchKernelGGL(kernel, grid, dim3(kW2 * kWave), 0, s, Q, K, V, out, static_cast<int>(nq),
+                       static_cast<int>(N), H, scale_log2, k3, m2);
   } else {
     const dim3 grid(static_cast<unsigned>((nq + kBM - 1) / kBM), static_cast<unsigned>(H));
     hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(kThreads), 0, s, Q, K, V, out,

@@ -264,10 +264,10 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
                                            static_cast<hipStream_t>(stream)));
 }
 
-int jano_attention_plan(int64_t n_q, int H, int d, int32_t *queries_per_workgroup) {
-  if (!queries_per_workgroup || n_q < 1 || H < 1 || n_q > kMaxRows) return JANO_E_INVAL;
+int jano_attention_plan(int64_t n_q, int H, int d, int32_t *tiles_per_head) {
+  if (!tiles_per_head || n_q < 1 || H < 1 || n_q > kMaxRows) return JANO_E_INVAL;
   if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
-  *queries_per_workgroup = jano::attention_tile_queries(n_q, H, d);
+  jano::attention_tiles(n_q, H, d, tiles_per_head);
   return JANO_OK;
 }
 

@@ -70,8 +70,9 @@ bool qkv_proj_supported(int64_t N, int64_t Dm, int H, int d);
 hipError_t launch_qkv_proj(const uint16_t *X, int64_t Dm, const int32_t *idx, int64_t n_act,
                            const uint16_t *W, int H, int d, int Ht, int Wt, float rope_base,
                            uint16_t *Q, uint16_t *Kn, uint16_t *Vn, hipStream_t s);
-// queries per workgroup the attention launch for (nq, H, d) uses
-int attention_tile_queries(int64_t nq, int H, int d);
+// query tiles per head of the attention launch for (nq, H, d): 384-query and
+// 256-query tiles (d = 128), 128-query tiles (d = 64)
+void attention_tiles(int64_t nq, int H, int d, int32_t tiles[3]);
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K,
                             const uint16_t *V, int64_t N, int H, int d, float scale,
                             uint16_t *out, hipStream_t s);

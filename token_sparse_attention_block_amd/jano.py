@@ -98,7 +98,7 @@ def lib():
             "jano_gather_rows": ([vp, i64, i64, vp, i64, vp, vp], i32),
             "jano_scatter_kv": ([vp, vp, vp, i64, vp, vp, i64, i64, vp], i32),
             "jano_attention": ([vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
-            "jano_attention_plan": ([i64, i32, i32, ctypes.POINTER(ctypes.c_int32)], i32),
+            "jano_attention_plan": ([i64, i32, i32, vp], i32),
             "jano_attn_step": ([vp, vp, vp, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
             "jano_check_idx": ([vp, i64, i64, vp, vp], i32),
         }
@@ -163,11 +163,12 @@ def analyze_workspace_bytes(spec: GridSpec) -> int:
     return lib().jano_analyze_workspace_bytes(ctypes.byref(g))
 
 
-def attention_plan(n_q, H, d) -> int:
-    """jano_attention_plan: queries per workgroup of the attention launch."""
-    q = ctypes.c_int32()
-    _check("jano_attention_plan", lib().jano_attention_plan(int(n_q), int(H), int(d), ctypes.byref(q)))
-    return q.value
+def attention_plan(n_q, H, d) -> tuple:
+    """jano_attention_plan: query tiles per head of the attention launch,
+    (384-query tiles, 256-query tiles, 128-query tiles)."""
+    t = (ctypes.c_int32 * 3)()
+    _check("jano_attention_plan", lib().jano_attention_plan(int(n_q), int(H), int(d), t))
+    return tuple(t)
 
 
 def schedule_count(level_tok_counts, T, W, Cd, periods, step) -> int:
