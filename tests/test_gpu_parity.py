@@ -134,6 +134,9 @@ def test_analyzer_configs(torch, cfg, signal):
     ((9, 2, 2, 8, 8), (1, 4, 4), (1, 1, 1)),       # K=9 -> generic kernel
     ((5, 2, 2, 12, 140), (1, 4, 70), (1, 2, 2)),   # block wider than a wave -> generic
     ((5, 2, 3, 9, 10), (1, 3, 5), (1, 1, 1)),      # odd block height -> generic
+    ((3, 2, 5, 20, 232), (1, 8, 16), (1, 2, 2)),   # 16-wide blocks, ragged last block column and row
+    ((8, 3, 6, 12, 64), (3, 8, 32), (1, 1, 1)),    # K=8, 32-wide blocks, 3-frame blocks
+    ((4, 2, 7, 13, 196), (1, 4, 4), (1, 1, 1)),    # one-row last block row, many W chunks
 ])
 def test_analyzer_shapes(torch, shape, block, patch):
     print("analyze shape", shape, block, flush=True)
@@ -142,6 +145,22 @@ def test_analyzer_shapes(torch, shape, block, patch):
     spec = jano.GridSpec(*shape, block=block, patch=patch)
     s, l, c = _analyze_gpu(torch, lat, spec)
     _check_analyzer(lat, spec, s, l, c)
+
+
+@pytest.mark.parametrize("cfg", [configs.V720, configs.TINY], ids=lambda c: c.name)
+def test_analyzer_unaligned_latents(torch, cfg):
+    # latents that start 4 bytes past a 16-byte boundary (a view into a larger
+    # buffer) score the same as aligned ones
+    lat = synth.latents(cfg, signal=True)
+    spec = jano.GridSpec.of(cfg)
+    buf = torch.empty(lat.size + 1, dtype=torch.float32, device="cuda")
+    view = buf[1:].view(lat.shape)
+    view.copy_(torch.from_numpy(lat))
+    assert view.data_ptr() % 16 == 4
+    scores, levels, counts = jano.analyze(view, spec, cfg.static_permille, cfg.moderate_permille)
+    torch.cuda.synchronize()
+    _check_analyzer(lat, spec, scores.cpu().numpy(), levels.cpu().numpy(), counts.cpu().numpy(),
+                    cfg.static_permille, cfg.moderate_permille)
 
 
 def test_analyzer_closed_forms(torch, golden):
