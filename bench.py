@@ -680,7 +680,49 @@ def measure_ceilings(torch, reps=10):
     torch.cuda.empty_cache()
     out = {"gemm_bf16_TFLOP/s": round(gemm, 2), "gemm_size": best_n, "copy_1GiB_GB/s": round(copy, 1)}
     out.update(loop)
+    out.update(measure_streaming(torch, reps))
     return out
+
+
+def measure_streaming(torch, reps=10):
+    """HBM rates of plain streaming on this part: the calibration library's
+    16-byte non-temporal copy (1 GiB read + 1 GiB written) and read (1 GiB),
+    best over a few grid sizes, each timed over `reps` back-to-back calls on
+    two alternating buffer pairs (4 GiB in all, far past the last-level cache)."""
+    import ctypes
+    from token_sparse_attention_block_amd import build as B
+    f = ctypes.CDLL(B.CALIB_LIB).jano_calib_stream
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    nbytes = 1 << 30
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b_ in bufs:
+        b_.fill_(1)
+    sink = torch.empty(8192 * 256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for mode, name, moved in ((0, "stream_copy_GB/s", 2 * nbytes), (1, "stream_read_GB/s", nbytes)):
+        best = 0.0
+        for wgs in (1024, 2048, 4096, 8192):
+            def call(i):
+                src, dst = bufs[2 * (i % 2)], bufs[2 * (i % 2) + 1]
+                if f(mode, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, wgs,
+                     ctypes.c_void_p(sink.data_ptr()), st) != 0:
+                    raise RuntimeError("jano_calib_stream failed")
+            for i in range(2):
+                call(i)
+            a, b = _ev(torch), _ev(torch)
+            a.record()
+            for i in range(reps):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9)
+        res[name] = round(best, 1)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def measure_mfma_loop(torch, iters=30000):
@@ -852,6 +894,12 @@ def main():
     for k in ("gather", "scatter", "analyze_scores"):
         if "GB/s" in kernels[k]:
             ceilings["%s_frac_of_copy" % k] = round(kernels[k]["GB/s"] / ceilings["copy_1GiB_GB/s"], 4)
+    # against plain streaming of the same kind: row copies read and write,
+    # the analyzer only reads
+    for k, c in (("gather", "stream_copy_GB/s"), ("scatter", "stream_copy_GB/s"),
+                 ("analyze_scores", "stream_read_GB/s")):
+        if "GB/s" in kernels[k] and ceilings.get(c):
+            ceilings["%s_frac_of_%s" % (k, c[:-5])] = round(kernels[k]["GB/s"] / ceilings[c], 4)
 
     cpu = None
     if not args.no_cpu:

@@ -17,9 +17,27 @@
  * Returns 0 on success, 1 for a bad argument (shape not 0 or 1, workgroups or
  * iters < 1, sink NULL; nothing is launched), 2 when the launch fails.
  * Buffers belong to the caller. The call is asynchronous.
+ *
+ * jano_calib_stream streams `bytes` bytes (a multiple of 16, buffers 16-byte
+ * aligned) with `workgroups` workgroups of 256 threads, grid-stride, four
+ * 16-byte non-temporal loads in flight per thread. Timed with events, it
+ * gives the HBM rate plain streaming reaches on the part.
+ *
+ *   mode 0  copy: dst[0 .. bytes) = src[0 .. bytes) (non-temporal stores);
+ *           sink unused
+ *   mode 1  read: src is read and summed per thread; dst unused; sink is a
+ *           device buffer of workgroups * 256 floats, written only in a case
+ *           that does not occur (it keeps the loads from being removed)
+ *
+ * Returns 0 on success, 1 for a bad argument (mode not 0 or 1, src NULL or
+ * misaligned, bytes 0 or not a multiple of 16, workgroups < 1, dst NULL or
+ * misaligned in mode 0, sink NULL in mode 1; nothing is launched), 2 when
+ * the launch fails. The buffers must not overlap.
  */
 #ifndef JANO_CALIB_H
 #define JANO_CALIB_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -27,6 +45,8 @@ extern "C" {
 
 int jano_calib_mfma_loop(int shape, int workgroups, int iters, float *sink, long long *cycles,
                          void *stream);
+int jano_calib_stream(int mode, const void *src, void *dst, size_t bytes, int workgroups, float *sink,
+                      void *stream);
 
 #ifdef __cplusplus
 }

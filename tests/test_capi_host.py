@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 def test_calib_library_exports_and_rejects():
     from token_sparse_attention_block_amd import build as B
     names = declared_functions(os.path.join(ROOT, "include", "jano_calib.h"))
-    assert names == ["jano_calib_mfma_loop"]
+    assert names == ["jano_calib_mfma_loop", "jano_calib_stream"]
     out = subprocess.run(["nm", "-D", "--defined-only", B.CALIB_LIB], capture_output=True,
                          text=True, check=True).stdout
     syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -57,6 +57,19 @@ def test_calib_library_exports_and_rejects():
     assert f(0, 0, 1, sink, None, None) == 1
     assert f(0, 1, 0, sink, None, None) == 1
     assert f(1, 1, 1, None, None, None) == 1
+    g = ctypes.CDLL(B.CALIB_LIB).jano_calib_stream
+    g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    buf = ctypes.c_void_p(0x1000)    # 16-byte aligned, never dereferenced
+    assert g(2, buf, buf, 16, 1, sink, None) == 1          # mode
+    assert g(0, None, buf, 16, 1, sink, None) == 1         # src NULL
+    assert g(0, ctypes.c_void_p(0x1004), buf, 16, 1, sink, None) == 1   # src misaligned
+    assert g(0, buf, buf, 0, 1, sink, None) == 1           # no bytes
+    assert g(0, buf, buf, 24, 1, sink, None) == 1          # not a multiple of 16
+    assert g(0, buf, buf, 16, 0, sink, None) == 1          # no workgroups
+    assert g(0, buf, None, 16, 1, sink, None) == 1         # copy without dst
+    assert g(1, buf, None, 16, 1, None, None) == 1         # read without sink
 
 
 def test_version_and_status_strings():

@@ -1,6 +1,7 @@
 """Builds libjano.so (HIP for gfx950) in-tree with hipcc, and beside it
-libjano_calib.so, the calibration kernel that measurements use to find the
-matrix-core rate the part sustains (not part of the Jano path), and
+libjano_calib.so, the calibration kernels that measurements use to find the
+matrix-core rate and the streaming HBM rates the part sustains (not part of
+the Jano path), and
 libjano_asan.so, the same library with its host code (argument checks,
 launch set-up) built with AddressSanitizer for host-only ABI tests. The
 device code of the ASan build is compiled as usual; only the host pass is
@@ -26,7 +27,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libjano.so")
 SOURCES = ["capi.hip", "analyze.hip", "schedule.hip", "rows.hip", "attention.hip", "proj.hip"]
 CALIB_LIB = os.path.join(LIBDIR, "libjano_calib.so")
-CALIB_SOURCES = ["calib/mfma_loop.hip"]
+CALIB_SOURCES = ["calib/mfma_loop.hip", "calib/stream.hip"]
 ASAN_LIB = os.path.join(LIBDIR, "libjano_asan.so")
 ASAN_OBJ = os.path.join(OBJ, "asan")
 # host pass only: each sanitizer flag goes to the host compiler alone
