@@ -638,6 +638,43 @@ def cpu_baseline(cfg, synth, Qb, Kb, Vb, spm, mpm, step_id, seconds_hint=15.0):
             "oracle_step_ms_extrapolated": round(step_ms, 1)}
 
 
+def time_vendor_attention(torch, shapes, reps=5):
+    """PyTorch's fused scaled-dot-product attention (its flash backend only;
+    the math fallback stays disabled) on the same shapes with random bf16
+    Q [1,H,n,d], K/V [1,H,N,d] in the layout it takes: the attention the
+    framework itself offers on this part, timed like this path (median of
+    `reps` after two warm calls). Returns {shape: {...}} or a note when the
+    backend is not available."""
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+    except ImportError as e:
+        return {"unavailable": str(e)}
+    out = {"backend": "torch.nn.functional.scaled_dot_product_attention, flash backend"}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    for name, nq, N, H, d in shapes:
+        q = torch.randn((1, H, nq, d), generator=g, device="cuda").to(torch.bfloat16)
+        k = torch.randn((1, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((1, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                for _ in range(2):
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                ev = [(_ev(torch), _ev(torch)) for _ in range(reps)]
+                for a, b in ev:
+                    a.record()
+                    torch.nn.functional.scaled_dot_product_attention(q, k, v)
+                    b.record()
+                torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(4.0 * nq * N * H * d / (ms * 1e-3) / 1e12, 2)}
+        except RuntimeError as e:
+            out[name] = {"unavailable": str(e).splitlines()[0][:200]}
+        del q, k, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_ceilings(torch, reps=10):
     """Ceilings re-measured on this part in this run, beside the published
     peaks: the best of two large square bf16 GEMMs through torch.matmul (the
@@ -859,6 +896,11 @@ def main():
         print("bench: QKV projection", file=sys.stderr, flush=True)
         proj = time_qkv_proj(torch, jano, cfg, p.idx[:n_act])
 
+    vendor_attn = None
+    if not args.no_extra:
+        print("bench: vendor attention", file=sys.stderr, flush=True)
+        vendor_attn = time_vendor_attention(torch, (("active", n_act, N, H, d), ("dense", N, N, H, d)))
+
     print("bench: write-back step", file=sys.stderr, flush=True)
     writeback = time_writeback(torch, jano, cfg, p.idx[:n_act])
 
@@ -941,6 +983,12 @@ def main():
         line["concat_layout"] = concat
     if proj is not None:
         line["qkv_proj"] = proj
+    if vendor_attn is not None:
+        for key, ours in (("active", achieved), ("dense", dense_tflops)):
+            if "TFLOP/s" in vendor_attn.get(key, {}):
+                vendor_attn[key]["this_kernel_TFLOP/s"] = round(ours, 2)
+                vendor_attn[key]["speedup_of_this_kernel"] = round(ours / vendor_attn[key]["TFLOP/s"], 3)
+        line["vendor_attention"] = vendor_attn
     line.update(extra)
     print(json.dumps(line), flush=True)
 
