@@ -18,9 +18,12 @@
  *     validated on the host before anything is enqueued; on a non-zero return
  *     nothing was launched and no output was written (except JANO_E_HIP,
  *     reported when a launch itself fails).
- *   - The library allocates no device memory and keeps no state between
- *     calls; calls on different streams may run concurrently as long as their
- *     outputs do not overlap.
+ *   - The library allocates no device memory at run time and keeps no state
+ *     between calls; calls on different streams may run concurrently as long
+ *     as their outputs do not overlap. The one exception is
+ *     jano_analyze_noalloc: its scratch array is a fixed part of the library,
+ *     one per GPU, and the library remembers that array's device address after
+ *     the first call on each device (see there).
  */
 #ifndef JANO_H
 #define JANO_H
@@ -121,7 +124,8 @@ int jano_analyze_scores(const float *lat, const jano_grid *g, float *scores, voi
  *                     sum_{k != 0} |DFT(L[K-1][c] restricted to the block)_k|^2 / n^2
  *                     with n the block's pixels inside the latent -- by
  *                     Parseval the population variance of those pixels, which
- *                     is what is computed (two passes in fp64)
+ *                     is what is computed (one pass of fp64 sums of each pixel's
+ *                     difference from the block's first pixel, and of its square)
  * Rank the scores with jano_levels exactly as the analyzer's. No workspace.
  * Deterministic. Errors: JANO_E_INVAL for null pointers or a bad grid.
  */
