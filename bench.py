@@ -469,19 +469,52 @@ def time_qkv_proj(torch, jano, cfg, idx, reps=5):
             "frac_of_vendor_same_shape": round(tf / vtf, 4)}
 
 
-def time_dense(torch, jano, Q, Kc, Vc, reps=20):
-    """Median over `reps` launches of dense attention (every token a query),
-    each launch between its own pair of events."""
+def time_dense(torch, jano, Q, Kc, Vc, reps=20, workspace=None):
+    """Median over `reps` launches of attention of the queries Q against the
+    whole cache (all tokens for the dense reference), each launch between its
+    own pair of events."""
     out = torch.empty_like(Q)
-    jano.attention(Q, Kc, Vc, out=out)
+    jano.attention(Q, Kc, Vc, out=out, workspace=workspace)
     torch.cuda.synchronize()
     ev = [(_ev(torch), _ev(torch)) for _ in range(reps)]
     for a, b in ev:
         a.record()
-        jano.attention(Q, Kc, Vc, out=out)
+        jano.attention(Q, Kc, Vc, out=out, workspace=workspace)
         b.record()
     torch.cuda.synchronize()
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_configs(torch, jano, synth, configs):
+    """Active-query attention on the smaller grids at their active shares
+    (the first n_act rows of the config's seeded Q against its whole K/V):
+    median of 20 launches each, as TFLOP/s and as a fraction of the bf16
+    peak (d = 64 for the tiny grid runs the d = 64 kernel); where the launch
+    splits the keys when given a workspace, also with one."""
+    out = {}
+    for cfg in (configs.TINY, configs.IMAGE, configs.V480):
+        Q, K, V = make_qkv(torch, synth, cfg)
+        N, H, d = cfg.N, cfg.heads, cfg.d
+        for frac in cfg.active_fracs:
+            n_act = max(1, round(frac * N))
+            Qa = Q[:n_act].contiguous()
+            flops = 4.0 * n_act * N * H * d
+            ms = time_dense(torch, jano, Qa, K, V, 20)
+            tf = flops / (ms * 1e-3) / 1e12
+            rec = {"tokens": N, "heads": H, "head_dim": d, "n_act": n_act, "ms": round(ms, 4),
+                   "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+            ws = jano.attention_workspace(n_act, N, H, d, "cuda")
+            if ws is not None:
+                ms_ws = time_dense(torch, jano, Qa, K, V, 20, workspace=ws)
+                tf_ws = flops / (ms_ws * 1e-3) / 1e12
+                rec["with_workspace"] = {"key_ranges": jano.attention_plan_ws(n_act, N, H, d)[3],
+                                         "workspace_MB": round(ws.numel() / 1e6, 2), "ms": round(ms_ws, 4),
+                                         "TFLOP/s": round(tf_ws, 2),
+                                         "frac_mfma": round(tf_ws / PEAK_BF16_TFLOPS, 4)}
+                del ws
+            out["%s-%d%%" % (cfg.name, round(100 * frac))] = rec
+        del Q, K, V
+    return out
 
 
 def sched_run(torch, jano, synth, cfg):
@@ -896,6 +929,11 @@ def main():
         print("bench: QKV projection", file=sys.stderr, flush=True)
         proj = time_qkv_proj(torch, jano, cfg, p.idx[:n_act])
 
+    per_config = None
+    if not args.no_extra:
+        print("bench: attention on the smaller grids", file=sys.stderr, flush=True)
+        per_config = time_configs(torch, jano, synth, configs)
+
     vendor_attn = None
     if not args.no_extra:
         print("bench: vendor attention", file=sys.stderr, flush=True)
@@ -983,6 +1021,8 @@ def main():
         line["concat_layout"] = concat
     if proj is not None:
         line["qkv_proj"] = proj
+    if per_config is not None:
+        line["attention_other_grids"] = per_config
     if vendor_attn is not None:
         for key, ours in (("active", achieved), ("dense", dense_tflops)):
             if "TFLOP/s" in vendor_attn.get(key, {}):

@@ -308,6 +308,46 @@ int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t 
                    int64_t N, int H, int d, float scale, uint16_t *out, void *stream);
 
 /*
+ * jano_attention_ws, jano_attn_step_ws -- jano_attention and jano_attn_step
+ * with an optional workspace. With one, a launch may split each head's keys
+ * into S key ranges handled by S workgroups each. It does so when its query
+ * tiles alone would leave the GPU's compute units idle for much of the
+ * launch (few queries, or a mostly empty last round). Each key range writes
+ * its partial result to ws: the unnormalised fp32 output, the running max and
+ * the row sum. A second launch merges the ranges in range order.
+ * Pages: as jano_attention / jano_attn_step (nl problem statement; nl
+ * methodology §2); the split is how this library fills the GPU.
+ *   ws, ws_bytes   NULL: exactly jano_attention / jano_attn_step. Otherwise
+ *                  a device buffer, 16-byte aligned, of at least
+ *                  jano_attention_workspace_bytes(n_q or n_act, N, H, d) bytes;
+ *                  contents need no initialisation. When that size is 0 the
+ *                  plan does not split and ws is not touched.
+ * Other arguments, layouts and results as there. A split launch sums over
+ * the keys in another order than the unsplit one, so the two differ by
+ * rounding; each is deterministic.
+ * Errors: as there, and JANO_E_WORKSPACE (nothing launched) when the plan
+ * splits and ws is too small or misaligned.
+ */
+int jano_attention_ws(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
+                      int64_t N, int H, int d, float scale, uint16_t *out, void *ws, size_t ws_bytes,
+                      void *stream);
+int jano_attn_step_ws(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
+                      const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
+                      int d, float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Host helper: bytes of workspace jano_attention_ws / jano_attn_step_ws need
+ * for n_q queries against N keys (0: the plan does not split; always 0 for
+ * d = 64 and for invalid sizes). */
+size_t jano_attention_workspace_bytes(int64_t n_q, int64_t N, int H, int d);
+
+/* Host helper: the plan of jano_attention_ws given a workspace.
+ *   plan (out) [4]: [0..2] tiles per head as jano_attention_plan reports them
+ *   (for a split plan, the one query-tile form it uses), [3] key ranges per
+ *   query tile (1: no split).
+ * Errors: JANO_E_INVAL (n_q, N or H below 1, null output), JANO_E_UNSUPPORTED (d). */
+int jano_attention_plan_ws(int64_t n_q, int64_t N, int H, int d, int32_t *plan);
+
+/*
  * jano_writeback_step -- write the active tokens' model output back and take
  * one sampler (Euler) step for every token.
  * Pages: nl "three groups" (the static group rests while its result is

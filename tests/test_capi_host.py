@@ -288,3 +288,38 @@ def test_attention_plan_tiles():
     assert L.jano_attention_plan(10, 0, 128, t) == jano.JANO_E_INVAL
     assert L.jano_attention_plan(10, 1, 96, t) == jano.JANO_E_UNSUPPORTED
     assert L.jano_attention_plan(10, 1, 128, None) == jano.JANO_E_INVAL
+
+
+def test_attention_split_plan_and_workspace():
+    # with a workspace: (384-query tiles, 256-query tiles, 128-query tiles, key ranges)
+    assert jano.attention_plan_ws(18468, 75600, 40, 128) == (44, 7, 0, 1)    # 7.7 rounds: no split
+    assert jano.attention_plan_ws(75600, 75600, 40, 128) == (197, 0, 0, 1)
+    assert jano.attention_plan_ws(8190, 32760, 12, 128) == (0, 32, 0, 2)     # 1.4 rounds -> 2 ranges
+    assert jano.attention_plan_ws(4096, 4096, 24, 128) == (0, 16, 0, 2)
+    assert jano.attention_plan_ws(100, 1000, 2, 128) == (0, 1, 0, 4)
+    assert jano.attention_plan_ws(10, 100, 1, 64) == (0, 0, 1, 1)            # d = 64 never splits
+    assert jano.attention_plan_ws(50, 100, 1, 128)[3] == 1                  # 2 tiles: too few to split
+    for n, N, H in ((8190, 32760, 12), (4096, 4096, 24), (100, 1000, 2), (3000, 500, 8)):
+        S = jano.attention_plan_ws(n, N, H, 128)[3]
+        assert S > 1 and -(-N // 64) >= 2 * S
+        assert jano.attention_workspace_bytes(n, N, H, 128) == S * n * H * 130 * 4
+    assert jano.attention_workspace_bytes(18468, 75600, 40, 128) == 0
+    assert jano.attention_workspace_bytes(10, 100, 1, 64) == 0
+    assert jano.attention_workspace_bytes(0, 100, 1, 128) == 0
+    L = jano.lib()
+    t = (ctypes.c_int32 * 4)()
+    assert L.jano_attention_plan_ws(10, 0, 1, 128, t) == jano.JANO_E_INVAL
+    assert L.jano_attention_plan_ws(10, 100, 1, 96, t) == jano.JANO_E_UNSUPPORTED
+    assert L.jano_attention_plan_ws(10, 100, 1, 128, None) == jano.JANO_E_INVAL
+    # workspace errors are reported before anything is enqueued (fake,
+    # never-dereferenced device pointers)
+    f = ctypes.c_void_p(0x1000)
+    n, N, H, d = 8190, 32760, 12, 128
+    need = jano.attention_workspace_bytes(n, N, H, d)
+    assert L.jano_attention_ws(f, n, f, f, N, H, d, 0.0, f, f, need - 16, None) == jano.JANO_E_WORKSPACE
+    assert L.jano_attention_ws(f, n, f, f, N, H, d, 0.0, f, ctypes.c_void_p(0x1008), need, None) == \
+        jano.JANO_E_WORKSPACE
+    assert L.jano_attn_step_ws(f, f, f, f, n, f, f, N, H, d, 0.0, f, f, 16, None) == jano.JANO_E_WORKSPACE
+    # the usual argument checks come first
+    assert L.jano_attention_ws(f, n, f, f, N, H, 96, 0.0, f, f, 0, None) == jano.JANO_E_UNSUPPORTED
+    assert L.jano_attention_ws(f, n, f, f, 0, H, d, 0.0, f, f, need, None) == jano.JANO_E_INVAL

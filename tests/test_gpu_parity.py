@@ -480,7 +480,7 @@ def _qkv(cfg, extra=0):
     return _QKV_MEMO[key]
 
 
-def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0):
+def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0, ws=False):
     Qb, Kb, Vb = _qkv(cfg, extra)
     if q_mult != 1.0:
         Qb = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(Qb) * np.float32(q_mult))
@@ -491,7 +491,13 @@ def _attn_case(torch, cfg, idx, sample=None, extra=0, q_mult=1.0):
     Kst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
     Vst[idx] = rng.integers(0, 65535, size=(len(idx), cfg.heads, cfg.d), dtype=np.uint16) & 0x3FFF
     Kc, Vc = dev_bf16(Kst), dev_bf16(Vst)
-    out = jano.attn_step(dev_bf16(Qb[idx]), dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev(idx), Kc, Vc)
+    workspace = None
+    if ws:
+        # with a workspace, these shapes' launches split the keys
+        assert jano.attention_plan_ws(len(idx), cfg.N, cfg.heads, cfg.d)[3] > 1
+        workspace = jano.attention_workspace(len(idx), cfg.N, cfg.heads, cfg.d, "cuda")
+    out = jano.attn_step(dev_bf16(Qb[idx]), dev_bf16(Kb[idx]), dev_bf16(Vb[idx]), dev(idx), Kc, Vc,
+                         workspace=workspace)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host_bits(Kc), Kb)
     np.testing.assert_array_equal(host_bits(Vc), Vb)
@@ -530,6 +536,73 @@ def test_attention_full_size_sampled(torch, cfg, frac):
     sample = _sample_rows(len(idx))
     got, ref = _attn_case(torch, cfg, idx, sample=sample)
     assert_attn_close(got, ref, "%s %.0f%% sampled" % (cfg.name, 100 * frac))
+
+
+@pytest.mark.parametrize("cfg,frac,sampled", [(configs.IMAGE, 0.3, False), (configs.IMAGE, 1.0, False),
+                                              (configs.V480, 0.25, True)],
+                         ids=["image-30", "image-100", "480p-25-sampled"])
+def test_attention_split_keys_configs(torch, cfg, frac, sampled):
+    # the steps whose launches split the keys when given a workspace
+    print("attention split", cfg.name, frac, flush=True)
+    idx = _idx_for(cfg, frac)
+    sample = _sample_rows(len(idx)) if sampled else None
+    got, ref = _attn_case(torch, cfg, idx, sample=sample, ws=True)
+    assert_attn_close(got, ref, "%s %.0f%% split" % (cfg.name, 100 * frac))
+
+
+# Given a workspace, a launch may split each head's keys into S ranges
+# (jano_attention_plan_ws): both query-tile forms with 2, 3 and 4 ranges,
+# ragged query tails, and the ragged key tile always in the last range.
+@pytest.mark.parametrize("n,N,H,plan", [
+    (50, 200, 1, (0, 1, 0, 2)), (3000, 500, 6, (0, 12, 0, 3)), (50, 500, 1, (0, 1, 0, 4)),
+    (3000, 200, 12, (8, 0, 0, 2)), (2000, 500, 12, (6, 0, 0, 3)), (3000, 500, 8, (8, 0, 0, 4))])
+def test_attention_split_keys(torch, n, N, H, plan):
+    print("attention split keys", n, N, H, flush=True)
+    d = 128
+    assert jano.attention_plan_ws(n, N, H, d) == plan
+    rng = np.random.default_rng(n + 3 * N + H)
+    Q = synth.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
+    K = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    V = synth.f32_to_bf16_bits(rng.standard_normal((N, H, d)).astype(np.float32))
+    ws = jano.attention_workspace(n, N, H, d, "cuda")
+    assert ws.numel() == plan[3] * n * H * 130 * 4
+    Qd, Kd, Vd = dev_bf16(Q), dev_bf16(K), dev_bf16(V)
+    out = jano.attention(Qd, Kd, Vd, workspace=ws)
+    again = jano.attention(Qd, Kd, Vd, workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Q), O.bf16_to_f64(K), O.bf16_to_f64(V))
+    assert_attn_close(host_bf16_f64(out), ref, "split n=%d N=%d H=%d" % (n, N, H))
+    np.testing.assert_array_equal(host_bits(again), host_bits(out))   # deterministic
+
+
+@pytest.mark.parametrize("case", ["mid-tile", "ragged-tail", "double"])
+def test_attention_split_keys_late_max(torch, case):
+    # the late-max inputs below (N = 1000: 15 tiles + 40 keys) in four key
+    # ranges of 4 tiles: the jumps land in ranges 1 and 3, so the ranges merge
+    # with different maxima
+    rng = np.random.default_rng(77)
+    n, N, H, d = 100, 1000, 2, 128
+    assert jano.attention_plan_ws(n, N, H, d)[3] == 4
+    c = 1.4426950408889634 / np.sqrt(d)
+    Q = 0.1 * rng.standard_normal((n, H, d)).astype(np.float32)
+    K = 0.1 * rng.standard_normal((N, H, d)).astype(np.float32)
+    V = rng.standard_normal((N, H, d)).astype(np.float32)
+    Q[:, :, 0] = 4.0
+    K[:, :, 0] = 0.0
+    up = np.float32(8.5 / (4.0 * c))
+    if case == "mid-tile":
+        K[448:512, :, 0] = up
+    elif case == "ragged-tail":
+        K[960:1000, :, 0] = up
+    else:
+        K[500, :, 0] = 40.0
+        K[990, :, 0] = 80.0
+    Qb, Kb, Vb = (synth.f32_to_bf16_bits(x) for x in (Q, K, V))
+    ws = jano.attention_workspace(n, N, H, d, "cuda")
+    out = jano.attention(dev_bf16(Qb), dev_bf16(Kb), dev_bf16(Vb), workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.attention(O.bf16_to_f64(Qb), O.bf16_to_f64(Kb), O.bf16_to_f64(Vb))
+    assert_attn_close(host_bf16_f64(out), ref, "split late max %s" % case)
 
 
 @pytest.mark.parametrize("cfg", [configs.V480, configs.V720], ids=["480p-dense", "720p-dense"])

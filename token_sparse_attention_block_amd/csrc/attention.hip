@@ -312,11 +312,17 @@ __device__ __forceinline__ void issue_tile_full(const char *kbase, const char *v
 // G query groups of 16 per wave: G = 3 (384 queries per workgroup) is the
 // fast form; G = 2 (256 per workgroup) loses some LDS reuse but fills the
 // last round of a launch whose 384-query tiles would leave most CUs idle.
-template <int G>
+// Keys: tiles [kt0, kt1) of 64 (the whole range unless the launch splits the
+// keys). part_o NULL: the normalised bf16 output goes to out. Otherwise the
+// key range's unnormalised fp32 output goes to part_o [nq][H][128] and its
+// running max (log2 units) and row sum to part_m and part_l [nq][H], for
+// combine_kernel to merge.
+template <int G, bool SPLIT>
 __device__ __forceinline__ void attn_tile_d128(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     uint16_t *__restrict__ out, int nq, int N, int H, float scale_log2, int head, int q0,
-    char (*lds)[2][kTileB]) {
+    char (*lds)[2][kTileB], int kt0, int kt1, float *__restrict__ part_o,
+    float *__restrict__ part_m, float *__restrict__ part_l) {
   constexpr int D = 128;
   constexpr int kQW2 = 16 * G;              // queries per wave
   // LDS fragment reads issued ahead of the MFMAs that use them: the 2-group
@@ -331,8 +337,12 @@ __device__ __forceinline__ void attn_tile_d128(
   const size_t rs = static_cast<size_t>(H) * D;
   const uint16_t *Kh = K + static_cast<size_t>(head) * D;
   const uint16_t *Vh = V + static_cast<size_t>(head) * D;
-  const int ntiles = (N + kBN - 1) / kBN;
-  const int nfull = N / kBN;
+  // local tiles 0 .. ntiles-1 are tiles kt0 .. kt1-1; the first nfull are
+  // whole (only the range that ends at N can end in a ragged tile). Without
+  // a split the range is every key.
+  const int ntiles = SPLIT ? kt1 - kt0 : (N + kBN - 1) / kBN;
+  const int nfull = SPLIT ? min(kt1, N / kBN) - kt0 : N / kBN;
+  if (!SPLIT) kt0 = 0;
   // byte offsets of this lane's two copies within a tile (row r, swizzled chunk)
   uint32_t koff[2], voff[2];
 #pragma unroll
@@ -346,11 +356,11 @@ __device__ __forceinline__ void attn_tile_d128(
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds[0][0]) + 8 * wave * kRowB);
   auto issue = [&](const int t, const int stg) {
     if (t < nfull)
-      issue_tile_full(reinterpret_cast<const char *>(Kh) + t * tile_bytes,
-                      reinterpret_cast<const char *>(Vh) + t * tile_bytes, koff, voff,
+      issue_tile_full(reinterpret_cast<const char *>(Kh) + (kt0 + t) * tile_bytes,
+                      reinterpret_cast<const char *>(Vh) + (kt0 + t) * tile_bytes, koff, voff,
                       lds0 + stg * 2 * kTileB, lds0 + stg * 2 * kTileB + kTileB);
     else
-      issue_tile(Kh, Vh, rs, N, t * kBN, lds[stg][0], lds[stg][1], wave, lane);
+      issue_tile(Kh, Vh, rs, N, (kt0 + t) * kBN, lds[stg][0], lds[stg][1], wave, lane);
   };
 
   issue(0, 0);
@@ -449,7 +459,7 @@ __device__ __forceinline__ void attn_tile_d128(
         for (int b = 0; b < kBN / 16; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (j * kBN + 16 * b + 4 * h4 + r >= N) s[g][b][r] = -INFINITY;
+            if ((kt0 + j) * kBN + 16 * b + 4 * h4 + r >= N) s[g][b][r] = -INFINITY;
       }
       // this lane's 16 keys of the query; the 4 lanes that share a query
       // exchange maxima only when one of them would raise the running max
@@ -520,6 +530,20 @@ __device__ __forceinline__ void attn_tile_d128(
   for (int g = 0; g < G; ++g) {
     float l_tot = l_run[g] + shfl_xor_f32(l_run[g], 16);
     l_tot += shfl_xor_f32(l_tot, 32);
+    if constexpr (SPLIT) {
+      // a key range's share: unnormalised output, its max and row sum
+      if (qrow[g] < nq) {
+        const size_t qh = static_cast<size_t>(qrow[g]) * H + head;
+        float *po = part_o + qh * D;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4v *>(po + 16 * db + 4 * h4) = o[g][db];
+        if (h4 == 0) {
+          part_m[qh] = m_run[g];
+          part_l[qh] = l_tot;
+        }
+      }
+      continue;
+    }
     const float inv = 1.0f / l_tot;
     if (qrow[g] < nq) {
       uint16_t *op = out + static_cast<size_t>(qrow[g]) * rs + static_cast<size_t>(head) * D;
@@ -554,11 +578,66 @@ __global__ __launch_bounds__(kW2 * kWave) void attn_fwd_d128_kernel(
   const int i = blockIdx.x, n3 = H * k3;
   if (FORM == 3 || (FORM == 0 && i < n3)) {
     const int t = xcd_order(i, n3);
-    attn_tile_d128<3>(Q, K, V, out, nq, N, H, scale_log2, t / k3, 384 * (t % k3), lds);
+    attn_tile_d128<3, false>(Q, K, V, out, nq, N, H, scale_log2, t / k3, 384 * (t % k3), lds, 0, 0, nullptr,
+                             nullptr, nullptr);
   } else {
     const int t = xcd_order(i - n3, H * m2);
-    attn_tile_d128<2>(Q, K, V, out, nq, N, H, scale_log2, t / m2, 384 * k3 + 256 * (t % m2), lds);
+    attn_tile_d128<2, false>(Q, K, V, out, nq, N, H, scale_log2, t / m2, 384 * k3 + 256 * (t % m2), lds, 0,
+                             0, nullptr, nullptr, nullptr);
   }
+}
+
+// Key-split launch: every (head, key range, query tile) is one workgroup of
+// the 384-query (G = 3) or 256-query (G = 2) form, numbered XCD by XCD with
+// the query tile fastest, so the workgroups that stream one head's key range
+// share an L2. Key range s of S holds tiles [s*nt/S, (s+1)*nt/S).
+template <int G>
+__global__ __launch_bounds__(kW2 * kWave) void attn_split_d128_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
+    int nq, int N, int H, float scale_log2, int tiles, int S, float *__restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages][2][kTileB];
+  const int t = xcd_order(blockIdx.x, H * S * tiles);
+  const int head = t / (S * tiles), sp = (t / tiles) % S, qt = t % tiles;
+  const int nt = (N + kBN - 1) / kBN;
+  const size_t nqh = static_cast<size_t>(nq) * H;
+  float *po = ws + static_cast<size_t>(sp) * nqh * 128;
+  float *pm = ws + static_cast<size_t>(S) * nqh * 128 + static_cast<size_t>(sp) * nqh;
+  float *pl = ws + static_cast<size_t>(S) * nqh * 129 + static_cast<size_t>(sp) * nqh;
+  attn_tile_d128<G, true>(Q, K, V, nullptr, nq, N, H, scale_log2, head, 16 * kW2 * G * qt, lds, sp * nt / S,
+                          (sp + 1) * nt / S, po, pm, pl);
+}
+
+// Merge of the S key ranges' partial results, in range order: with m the
+// largest range max, out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s.
+// One thread per 8 output dims of one (query, head).
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *__restrict__ ws, int nq, int H,
+                                                                  int S, uint16_t *__restrict__ out) {
+  const size_t nqh = static_cast<size_t>(nq) * H;
+  const size_t i = static_cast<size_t>(blockIdx.x) * kCombineThreads + threadIdx.x;
+  if (i >= nqh * 16) return;
+  const size_t qh = i / 16;
+  const int c = static_cast<int>(i % 16);
+  const float *pm = ws + static_cast<size_t>(S) * nqh * 128;
+  const float *pl = pm + static_cast<size_t>(S) * nqh;
+  float m = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, pm[sp * nqh + qh]);
+  float l = 0.0f, acc[8] = {};
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = __builtin_amdgcn_exp2f(pm[sp * nqh + qh] - m);
+    l += w * pl[sp * nqh + qh];
+    const f32x4v *po = reinterpret_cast<const f32x4v *>(ws + (static_cast<size_t>(sp) * nqh + qh) * 128 + 8 * c);
+    const f32x4v a = po[0], b = po[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += w * a[e];
+      acc[4 + e] += w * b[e];
+    }
+  }
+  const float inv = 1.0f / l;
+  const f32x8 v = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
+                   acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  *reinterpret_cast<bf16x8 *>(out + qh * 128 + 8 * c) = __builtin_convertvector(v, bf16x8);
 }
 
 // Tiles of the d = 128 kernel for one launch. One workgroup fills a CU
@@ -621,7 +700,63 @@ void plan_d128(int64_t nq, int H, int *k3, int *m2) {
   *m2 = static_cast<int>(bm);
 }
 
+// Key-split plan, used only when the caller provides a workspace: each
+// (head, query tile) is split into S key ranges (S workgroups of 1/S the
+// work each) and a combine launch merges them. Modelled like plan_d128, a
+// launch of one tile form finishes after ceil(per-XCD workgroups / 32)
+// rounds of cost/S; a split plan is taken only when it beats the best
+// unsplit plan by more than 15% (the combine, the per-workgroup prologue and
+// the partial writes are not in the model). Each key range keeps >= 2 tiles.
+constexpr int kMaxSplit = 4;
+constexpr double kSplitMargin = 1.15;
+
+void plan_split_d128(int64_t nq, int64_t N, int H, int *G, int *tiles, int *S) {
+  int k3, m2;
+  plan_d128(nq, H, &k3, &m2);
+  const double f1 = plan_finish(k3, m2, H);
+  const int64_t nt = (N + kBN - 1) / kBN;
+  double best = f1 / kSplitMargin;
+  *S = 1;
+  *G = 0;
+  *tiles = 0;
+  for (int g = 3; g >= 2; --g) {
+    const int64_t qt = (nq + 128 * g - 1) / (128 * g);
+    const double cost = g == 3 ? 1.0 : kCostG2;
+    for (int sp = 2; sp <= kMaxSplit; ++sp) {
+      if (nt < 2 * sp) break;
+      const int64_t per_xcd = (static_cast<int64_t>(H) * qt * sp + kXcdsAttn - 1) / kXcdsAttn;
+      const double f = static_cast<double>((per_xcd + kCUsPerXcd - 1) / kCUsPerXcd) * cost / sp;
+      if (f < best - 1e-9) {
+        best = f;
+        *S = sp;
+        *G = g;
+        *tiles = static_cast<int>(qt);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+size_t attention_ws_bytes(int64_t nq, int64_t N, int H, int d) {
+  if (d != 128 || nq < 1 || N < 1 || H < 1) return 0;
+  int G, tiles, S;
+  plan_split_d128(nq, N, H, &G, &tiles, &S);
+  return S > 1 ? static_cast<size_t>(S) * nq * H * 130 * sizeof(float) : 0;
+}
+
+void attention_tiles_ws(int64_t nq, int64_t N, int H, int d, int32_t plan[4]) {
+  attention_tiles(nq, H, d, plan);
+  plan[3] = 1;
+  if (d != 128) return;
+  int G, tiles, S;
+  plan_split_d128(nq, N, H, &G, &tiles, &S);
+  if (S > 1) {
+    plan[0] = G == 3 ? tiles : 0;
+    plan[1] = G == 2 ? tiles : 0;
+    plan[3] = S;
+  }
+}
 
 void attention_tiles(int64_t nq, int H, int d, int32_t tiles[3]) {
   tiles[0] = tiles[1] = tiles[2] = 0;
@@ -636,9 +771,28 @@ void attention_tiles(int64_t nq, int H, int d, int32_t tiles[3]) {
 }
 
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K, const uint16_t *V,
-                            int64_t N, int H, int d, float scale, uint16_t *out, hipStream_t s) {
+                            int64_t N, int H, int d, float scale, uint16_t *out, float *ws, hipStream_t s) {
   if (nq == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
+  if (d == 128 && ws != nullptr) {
+    int G, tiles, S;
+    plan_split_d128(nq, N, H, &G, &tiles, &S);
+    if (S > 1) {
+      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(H) * tiles * S));
+      if (G == 3)
+        hipLaunchKernelGGL(attn_split_d128_kernel<3>, grid, dim3(kW2 * kWave), 0, s, Q, K, V,
+                           static_cast<int>(nq), static_cast<int>(N), H, scale_log2, tiles, S, ws);
+      else
+        hipLaunchKernelGGL(attn_split_d128_kernel<2>, grid, dim3(kW2 * kWave), 0, s, Q, K, V,
+                           static_cast<int>(nq), static_cast<int>(N), H, scale_log2, tiles, S, ws);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t nthreads = nq * H * 16;
+      hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((nthreads + kCombineThreads - 1) / kCombineThreads)),
+                         dim3(kCombineThreads), 0, s, ws, static_cast<int>(nq), H, S, out);
+      return hipGetLastError();
+    }
+  }
   if (d == 128) {
     int k3, m2;
     plan_d128(nq, H, &k3, &m2);

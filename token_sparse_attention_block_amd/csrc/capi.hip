@@ -249,8 +249,22 @@ int jano_scatter_kv(const uint16_t *K_new, const uint16_t *V_new, const int32_t 
                                             static_cast<hipStream_t>(stream)));
 }
 
-int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
-                   int64_t N, int H, int d, float scale, uint16_t *out, void *stream) {
+// the key-split workspace of an attention launch: NULL selects the plain
+// launch; otherwise it must hold the plan's bytes (none when it does not split)
+static int check_attention_ws(int64_t n_q, int64_t N, int H, int d, const void *ws, size_t ws_bytes,
+                              float **wsf) {
+  *wsf = nullptr;
+  if (ws == nullptr) return JANO_OK;
+  const size_t need = jano::attention_ws_bytes(n_q, N, H, d);
+  if (need == 0) return JANO_OK;
+  if (ws_bytes < need || !aligned16(ws)) return JANO_E_WORKSPACE;
+  *wsf = static_cast<float *>(const_cast<void *>(ws));
+  return JANO_OK;
+}
+
+int jano_attention_ws(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
+                      int64_t N, int H, int d, float scale, uint16_t *out, void *ws, size_t ws_bytes,
+                      void *stream) {
   if (N < 1 || H < 1 || n_q < 0 || N > kMaxRows || n_q > kMaxRows || !isfinite(scale))
     return JANO_E_INVAL;
   if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
@@ -259,9 +273,29 @@ int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uin
   if (!aligned16(Q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(out)) return JANO_E_INVAL;
   if (H > 65535) return JANO_E_UNSUPPORTED;
   if (n_q == 0) return JANO_OK;
+  float *wsf;
+  const int w = check_attention_ws(n_q, N, H, d, ws, ws_bytes, &wsf);
+  if (w != JANO_OK) return w;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
-  return hip_status(jano::launch_attention(Q, n_q, Kc, Vc, N, H, d, sc, out,
+  return hip_status(jano::launch_attention(Q, n_q, Kc, Vc, N, H, d, sc, out, wsf,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int jano_attention(const uint16_t *Q, int64_t n_q, const uint16_t *Kc, const uint16_t *Vc,
+                   int64_t N, int H, int d, float scale, uint16_t *out, void *stream) {
+  return jano_attention_ws(Q, n_q, Kc, Vc, N, H, d, scale, out, nullptr, 0, stream);
+}
+
+size_t jano_attention_workspace_bytes(int64_t n_q, int64_t N, int H, int d) {
+  if (n_q < 1 || N < 1 || H < 1 || n_q > kMaxRows || N > kMaxRows || H > 65535) return 0;
+  return jano::attention_ws_bytes(n_q, N, H, d);
+}
+
+int jano_attention_plan_ws(int64_t n_q, int64_t N, int H, int d, int32_t *plan) {
+  if (!plan || n_q < 1 || N < 1 || H < 1 || n_q > kMaxRows || N > kMaxRows) return JANO_E_INVAL;
+  if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
+  jano::attention_tiles_ws(n_q, N, H, d, plan);
+  return JANO_OK;
 }
 
 int jano_attention_plan(int64_t n_q, int H, int d, int32_t *tiles_per_head) {
@@ -271,9 +305,9 @@ int jano_attention_plan(int64_t n_q, int H, int d, int32_t *tiles_per_head) {
   return JANO_OK;
 }
 
-int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
-                   const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
-                   int d, float scale, uint16_t *out, void *stream) {
+int jano_attn_step_ws(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
+                      const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
+                      int d, float scale, uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
   if (N < 1 || H < 1 || n_act < 0 || n_act > N || N > kMaxRows || !isfinite(scale))
     return JANO_E_INVAL;
   if (d != 64 && d != 128) return JANO_E_UNSUPPORTED;
@@ -282,12 +316,22 @@ int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t 
   if (n_act == 0) return JANO_OK;
   if (!Q_act || !K_new || !V_new || !idx || !out) return JANO_E_INVAL;
   if (!aligned16(Q_act) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(out)) return JANO_E_INVAL;
+  float *wsf;
+  const int w = check_attention_ws(n_act, N, H, d, ws, ws_bytes, &wsf);
+  if (w != JANO_OK) return w;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t HD = static_cast<int64_t>(H) * d;
   hipError_t e = jano::launch_scatter_kv(K_new, V_new, idx, n_act, Kc, Vc, HD, s);
   if (e != hipSuccess) return JANO_E_HIP;
   const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
-  return hip_status(jano::launch_attention(Q_act, n_act, Kc, Vc, N, H, d, sc, out, s));
+  return hip_status(jano::launch_attention(Q_act, n_act, Kc, Vc, N, H, d, sc, out, wsf, s));
+}
+
+int jano_attn_step(const uint16_t *Q_act, const uint16_t *K_new, const uint16_t *V_new,
+                   const int32_t *idx, int64_t n_act, uint16_t *Kc, uint16_t *Vc, int64_t N, int H,
+                   int d, float scale, uint16_t *out, void *stream) {
+  return jano_attn_step_ws(Q_act, K_new, V_new, idx, n_act, Kc, Vc, N, H, d, scale, out, nullptr, 0,
+                           stream);
 }
 
 int jano_qkv_proj(const uint16_t *X, int64_t N, int64_t Dm, const int32_t *idx, int64_t n_act,

@@ -73,8 +73,15 @@ hipError_t launch_qkv_proj(const uint16_t *X, int64_t Dm, const int32_t *idx, in
 // query tiles per head of the attention launch for (nq, H, d): 384-query and
 // 256-query tiles (d = 128), 128-query tiles (d = 64)
 void attention_tiles(int64_t nq, int H, int d, int32_t tiles[3]);
+// with a workspace: plan[0..2] as attention_tiles, plan[3] the key ranges per
+// query tile (1: no split); bytes of workspace that plan needs (0: none)
+void attention_tiles_ws(int64_t nq, int64_t N, int H, int d, int32_t plan[4]);
+size_t attention_ws_bytes(int64_t nq, int64_t N, int H, int d);
+// ws NULL: one launch, every workgroup over all keys; otherwise (d = 128) the
+// keys may be split over workgroups per the plan, partials in ws (of at least
+// attention_ws_bytes) and a combine launch
 hipError_t launch_attention(const uint16_t *Q, int64_t nq, const uint16_t *K,
                             const uint16_t *V, int64_t N, int H, int d, float scale,
-                            uint16_t *out, hipStream_t s);
+                            uint16_t *out, float *ws, hipStream_t s);
 
 }  // namespace jano

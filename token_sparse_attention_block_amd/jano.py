@@ -28,6 +28,7 @@ EXPORTS = (
     "jano_schedule", "jano_schedule_frozen", "jano_concat_kv", "jano_gather_rows",
     "jano_writeback_step", "jano_qkv_proj",
     "jano_scatter_kv", "jano_attention", "jano_attention_plan", "jano_attn_step", "jano_check_idx",
+    "jano_attention_ws", "jano_attn_step_ws", "jano_attention_workspace_bytes", "jano_attention_plan_ws",
 )
 
 
@@ -100,6 +101,11 @@ def lib():
             "jano_attention": ([vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
             "jano_attention_plan": ([i64, i32, i32, vp], i32),
             "jano_attn_step": ([vp, vp, vp, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp], i32),
+            "jano_attention_ws": ([vp, i64, vp, vp, i64, i32, i32, f32, vp, vp, ctypes.c_size_t, vp], i32),
+            "jano_attn_step_ws": ([vp, vp, vp, vp, i64, vp, vp, i64, i32, i32, f32, vp, vp, ctypes.c_size_t,
+                                   vp], i32),
+            "jano_attention_workspace_bytes": ([i64, i64, i32, i32], ctypes.c_size_t),
+            "jano_attention_plan_ws": ([i64, i64, i32, i32, vp], i32),
             "jano_check_idx": ([vp, i64, i64, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -169,6 +175,27 @@ def attention_plan(n_q, H, d) -> tuple:
     t = (ctypes.c_int32 * 3)()
     _check("jano_attention_plan", lib().jano_attention_plan(int(n_q), int(H), int(d), t))
     return tuple(t)
+
+
+def attention_plan_ws(n_q, N, H, d) -> tuple:
+    """jano_attention_plan_ws: the plan of an attention launch given a
+    workspace, (384-query tiles, 256-query tiles, 128-query tiles, key
+    ranges per query tile)."""
+    t = (ctypes.c_int32 * 4)()
+    _check("jano_attention_plan_ws", lib().jano_attention_plan_ws(int(n_q), int(N), int(H), int(d), t))
+    return tuple(t)
+
+
+def attention_workspace_bytes(n_q, N, H, d) -> int:
+    """jano_attention_workspace_bytes: workspace the key-split plan needs (0: none)."""
+    return int(lib().jano_attention_workspace_bytes(int(n_q), int(N), int(H), int(d)))
+
+
+def attention_workspace(n_q, N, H, d, device):
+    """A workspace for attention(..., workspace=) / attn_step(..., workspace=)
+    sized for this shape (None when the plan does not split)."""
+    n = attention_workspace_bytes(n_q, N, H, d)
+    return _torch().empty(n, dtype=_torch().uint8, device=device) if n else None
 
 
 def schedule_count(level_tok_counts, T, W, Cd, periods, step) -> int:
@@ -351,8 +378,10 @@ def _attn_shapes(Q, Kc, Vc, n):
     return N, H, d
 
 
-def attention(Q, Kc, Vc, scale=0.0, out=None, n_q=None):
-    """jano_attention: softmax(Q K^T * scale) V per head over all N cache rows."""
+def attention(Q, Kc, Vc, scale=0.0, out=None, n_q=None, workspace=None):
+    """jano_attention: softmax(Q K^T * scale) V per head over all N cache rows.
+    With a workspace (uint8 on the device, see attention_workspace) the call is
+    jano_attention_ws, which may split the keys over workgroups."""
     torch = _torch()
     n = Q.shape[0] if n_q is None else int(n_q)
     N, H, d = _attn_shapes(Q, Kc, Vc, n)
@@ -360,14 +389,21 @@ def attention(Q, Kc, Vc, scale=0.0, out=None, n_q=None):
     _need(out, "out", torch.bfloat16, None, Kc.device)
     if out.shape[0] < n or tuple(out.shape[1:]) != (H, d):
         raise ValueError("out must be [>= n, H, d]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, Kc.device)
+        _check("jano_attention_ws", lib().jano_attention_ws(
+            _ptr(Q), n, _ptr(Kc), _ptr(Vc), N, H, d, float(scale), _ptr(out), _ptr(workspace),
+            workspace.numel(), _stream(Kc)))
+        return out
     _check("jano_attention", lib().jano_attention(_ptr(Q), n, _ptr(Kc), _ptr(Vc), N, H, d,
                                                   float(scale), _ptr(out), _stream(Kc)))
     return out
 
 
-def attn_step(Q_act, K_new, V_new, idx, Kc, Vc, scale=0.0, out=None, n_act=None):
+def attn_step(Q_act, K_new, V_new, idx, Kc, Vc, scale=0.0, out=None, n_act=None, workspace=None):
     """jano_attn_step: scatter the fresh K/V rows into the cache, then
-    attention of the active queries against the whole cache."""
+    attention of the active queries against the whole cache. With a workspace
+    the call is jano_attn_step_ws (keys may be split over workgroups)."""
     torch = _torch()
     n = idx.numel() if n_act is None else int(n_act)
     N, H, d = _attn_shapes(Q_act, Kc, Vc, n)
@@ -383,6 +419,12 @@ def attn_step(Q_act, K_new, V_new, idx, Kc, Vc, scale=0.0, out=None, n_act=None)
     _need(out, "out", torch.bfloat16, None, dev)
     if out.shape[0] < n or tuple(out.shape[1:]) != (H, d):
         raise ValueError("out must be [>= n_act, H, d]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, dev)
+        _check("jano_attn_step_ws", lib().jano_attn_step_ws(
+            _ptr(Q_act), _ptr(K_new), _ptr(V_new), _ptr(idx), n, _ptr(Kc), _ptr(Vc), N, H, d,
+            float(scale), _ptr(out), _ptr(workspace), workspace.numel(), _stream(Kc)))
+        return out
     _check("jano_attn_step", lib().jano_attn_step(
         _ptr(Q_act), _ptr(K_new), _ptr(V_new), _ptr(idx), n, _ptr(Kc), _ptr(Vc), N, H, d,
         float(scale), _ptr(out), _stream(Kc)))
