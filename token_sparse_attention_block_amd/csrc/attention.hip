@@ -265,6 +265,10 @@ constexpr int kXcdsAttn = 8;    // accelerator dies (each with an L2) per GPU
 //   groups.
 //   Workgroups are renumbered so that each XCD (one L2 each) works through
 //   whole heads and the workgroups of a head share its K/V stream in one L2.
+//   The two waves that share a SIMD (w and w + 4) take a tile's work in
+//   different orders -- S, softmax, PV against PV of the previous tile, S,
+//   softmax -- and MFMA phases run at a higher wave priority than the
+//   softmax, so one wave's exponents overlap the other's MFMAs.
 //   The running max is raised only when a tile's max exceeds it by more than
 //   2^8 (kRescaleSlack), so most tiles skip the O rescale; P <= 2^8 stays well
 //   inside bf16 and fp32 range, and the final division by the row sum cancels
@@ -307,6 +311,22 @@ __device__ __forceinline__ void issue_tile_full(const char *kbase, const char *v
     copy16_to_lds_s(kbase, koff[i], lds_k + 4 * i * kRowB);
     copy16_to_lds_s(vbase, voff[i], lds_v + 4 * i * kRowB);
   }
+}
+
+// Wave priority around the two kinds of work of a tile, fenced so that the
+// compiler keeps each phase's instructions inside it. With one wave of a
+// SIMD in its MFMA phase and the other in its softmax, the arbiter serves the
+// MFMA wave first, so each MFMA issues as soon as the matrix core takes it
+// and the softmax's VALU instructions fill the cycles in between.
+__device__ __forceinline__ void matrix_phase() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void vector_phase() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // G query groups of 16 per wave: G = 3 (384 queries per workgroup) is the
@@ -411,18 +431,21 @@ __device__ __forceinline__ void attn_tile_d128(
     l_run[g] = 0.0f;
   }
 
-  // one 64-key tile; RAGGED only for a last tile that extends past N
-  auto tile = [&](const int j, auto ragged_tag) {
-    constexpr bool RAGGED = decltype(ragged_tag)::value;
-    const int st = j % kStages;
+  // tile j's K/V in LDS for every wave; tile j+2's copies issued
+  auto sync = [&](const int j) {
     if (j + 1 < ntiles)
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
     else
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
     if (j + 2 < ntiles) issue(j + 2, (j + 2) % kStages);
-    const char *kb = lds[st][0];
-    const char *vb = lds[st][1];
+  };
+  // S and softmax of one 64-key tile into pb; RAGGED only for a last tile
+  // that extends past N
+  auto s_soft = [&](const int j, auto ragged_tag, bf16x8 (&pb)[G][kBN / 32]) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
+    const char *kb = lds[j % kStages][0];
+    matrix_phase();
 
     f32x4v s[G][kBN / 16];
 #pragma unroll
@@ -450,8 +473,8 @@ __device__ __forceinline__ void attn_tile_d128(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kSAhead * G, 0);  // last MFMAs
+    vector_phase();
 
-    bf16x8 pb[G][kBN / 32];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if constexpr (RAGGED) {
@@ -498,7 +521,11 @@ __device__ __forceinline__ void attn_tile_d128(
       }
       l_run[g] += ls[0] + ls[1];
     }
-
+  };
+  // O += V^T P of the tile in stage st
+  auto pv = [&](const int st, const bf16x8 (&pb)[G][kBN / 32]) {
+    const char *vb = lds[st][1];
+    matrix_phase();
 #pragma unroll
     for (int ks = 0; ks < kBN / 32; ++ks)
 #pragma unroll
@@ -522,9 +549,48 @@ __device__ __forceinline__ void attn_tile_d128(
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kPVAhead * G, 1);
     }
+    vector_phase();
   };
-  for (int j = 0; j < nfull; ++j) tile(j, std::false_type{});
-  if (nfull < ntiles) tile(nfull, std::true_type{});
+  // Waves w and w + 4 share a SIMD. Waves 0-3 run S, softmax and PV of each
+  // tile; waves 4-7 run PV of the previous tile, then S and softmax of this
+  // one, carrying P over the barrier (the previous tile's V stays in its
+  // stage until the next tile's copies are issued, one barrier later). After
+  // the barrier both waves of a SIMD issue MFMAs; then one wave's softmax
+  // meets the other's S MFMAs, and the other's softmax meets the first
+  // one's PV MFMAs. P of the previous tile is dead before S of this tile is
+  // live, so the second order needs no more registers than the first.
+  if (__builtin_amdgcn_readfirstlane(wave) < kW2 / 2) {
+    for (int j = 0; j < nfull; ++j) {
+      sync(j);
+      bf16x8 pb[G][kBN / 32];
+      s_soft(j, std::false_type{}, pb);
+      pv(j % kStages, pb);
+    }
+    if (nfull < ntiles) {
+      sync(nfull);
+      bf16x8 pb[G][kBN / 32];
+      s_soft(nfull, std::true_type{}, pb);
+      pv(nfull % kStages, pb);
+    }
+  } else {
+    bf16x8 pb[G][kBN / 32];
+    if (nfull > 0) {
+      sync(0);
+      s_soft(0, std::false_type{}, pb);
+      for (int j = 1; j < nfull; ++j) {
+        sync(j);
+        pv((j - 1) % kStages, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        s_soft(j, std::false_type{}, pb);
+      }
+    }
+    if (nfull < ntiles) {
+      sync(nfull);
+      if (nfull > 0) pv((nfull - 1) % kStages, pb);
+      s_soft(nfull, std::true_type{}, pb);
+    }
+    pv((ntiles - 1) % kStages, pb);
+  }
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
