@@ -106,3 +106,16 @@ def test_cpu_baseline_runs_every_leg_on_a_small_workload():
     assert set(got["oracle_ms"]) == {"analyze_scores", "levels", "schedule", "gather", "scatter"}
     assert got["oracle_step_ms_extrapolated"] >= got["oracle_attention_ms_extrapolated"]
     assert got["cores"] >= 1
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    # the path runs on one GPU; asking for more exits before touching a device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
