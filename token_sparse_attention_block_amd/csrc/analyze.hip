@@ -47,7 +47,8 @@
 namespace jano {
 namespace {
 
-constexpr int kAnalyzeWaves = 4;          // waves per workgroup of kernel 1
+constexpr int kAnalyzeWaves = 1;          // waves per workgroup of kernel 1 (single-wave
+                                          // workgroups refill freed slots at the finest grain)
 constexpr int kXcds = 8;                  // accelerator dies (each with an L2) per GPU
 constexpr int kRankThreads = 1024;        // kernel 3 workgroup size
 constexpr int kRankSplit = 32;            // kernel 3 threads per block (one per 16 bytes of a 512-byte row)
