@@ -559,6 +559,9 @@ __device__ __forceinline__ void attn_tile_d128(
   // meets the other's S MFMAs, and the other's softmax meets the first
   // one's PV MFMAs. P of the previous tile is dead before S of this tile is
   // live, so the second order needs no more registers than the first.
+  // Both orders pass exactly ntiles barriers (sync), which is what keeps the
+  // workgroup's barrier count matched. Which waves share a SIMD decides only
+  // how well the phases overlap, never the result.
   if (__builtin_amdgcn_readfirstlane(wave) < kW2 / 2) {
     for (int j = 0; j < nfull; ++j) {
       sync(j);
