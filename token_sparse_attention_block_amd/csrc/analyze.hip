@@ -432,7 +432,7 @@ hipError_t launch_stream_r(const float *lat, const AnalyzeGeom &g, double *part,
 // 16-byte aligned rows). Each block's channel sum is taken in channel order
 // from LDS, so the result is deterministic.
 // ---------------------------------------------------------------------------
-constexpr int kFftThreads = 256;
+constexpr int kFftThreads = 512;           // one pass over a 720p block row's 320 (channel, column) pairs
 constexpr int kFftCols = 1024;             // block columns per pass over a block row
 constexpr int kFftPairs = 2048;            // (channel, block column) variances held in LDS
 
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_scores_kernel(const float *__
         const double x0 = static_cast<double>(Lc[static_cast<size_t>(f0) * plane]);
         double s1 = 0.0, s2 = 0.0;
         for (int f = f0; f < f1; ++f) {
-#pragma unroll 4
+#pragma unroll 8
           for (int h = 0; h < h1 - h0; ++h) {
             const float *row = Lc + f * plane + static_cast<size_t>(h) * g.W;
             if constexpr (VEC) {
